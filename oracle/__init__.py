@@ -1,0 +1,195 @@
+"""CPU oracle for the chunked AllGather + bf16 GEMM path and for TGATHER (ctypes binding).
+
+TEST INFRASTRUCTURE ONLY.  The test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg
+of ``bench.py`` may import this package; the GPU library (``allgather_gemm_amd``) never does and
+shares no code with it.  The arithmetic lives in ``oracle.c``; this module only builds the
+shared object with gcc and marshals numpy arrays.
+
+Pages followed (see oracle.h): the fused AllGather+MatMul article ("Triton第四课：基于对称内存融合
+AllGather 与 MatMul，提速1.56倍") and the TGATHER deep dive ("CANN PTO-ISA TGATHER 指令深度解析").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_SO = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+_i64 = ctypes.c_int64
+_vp = ctypes.c_void_p
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc into liboracle.so next to it and return its path."""
+    if force or not os.path.exists(_SO):
+        tmp = _SO + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-std=c11",
+               "-Wall", "-Wextra", "-shared", "-fPIC", _SRC, "-o", tmp]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _SO)
+    return _SO
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_SO):
+            build()
+        L = ctypes.CDLL(_SO)
+        L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
+        L.oracle_bf16_to_f32.restype = ctypes.c_float
+        L.oracle_f32_to_bf16_rne.argtypes = [ctypes.c_float]
+        L.oracle_f32_to_bf16_rne.restype = ctypes.c_uint16
+        L.oracle_tgather.argtypes = [_vp, ctypes.c_int, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
+                                     ctypes.c_int]
+        L.oracle_tgather.restype = ctypes.c_int
+        L.oracle_gemm_f32.argtypes = [_vp, _vp, _i64, _i64, _i64, _vp]
+        L.oracle_gemm_f32.restype = None
+        L.oracle_ag_gemm_at.argtypes = [_vp, ctypes.c_int, _i64, _i64, _vp, _i64, _vp, _vp, _i64,
+                                        _vp]
+        L.oracle_ag_gemm_at.restype = ctypes.c_int
+        L.oracle_ag_gemm.argtypes = [_vp, ctypes.c_int, _i64, _i64, _vp, _i64, _vp, _vp]
+        L.oracle_ag_gemm.restype = ctypes.c_int
+        L.oracle_chunk_of_row.argtypes = [_i64, _i64, _i64]
+        L.oracle_chunk_of_row.restype = _i64
+        L.oracle_chunks_overlapping.argtypes = [_i64, _i64, _i64, _i64, _vp, _i64]
+        L.oracle_chunks_overlapping.restype = _i64
+        L.oracle_grouped_tile.argtypes = [_i64, _i64, _i64, _i64, _vp, _vp]
+        L.oracle_grouped_tile.restype = None
+        L.oracle_ag_gemm_pivoted.argtypes = [_vp, ctypes.c_int, _i64, _i64, _vp, _i64, _i64, _i64,
+                                             _i64, _i64, ctypes.c_int, _vp, _vp, _vp]
+        L.oracle_ag_gemm_pivoted.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    assert a.flags.c_contiguous
+    return a.ctypes.data
+
+
+def _ptr_array(arrs) -> ctypes.Array:
+    return (ctypes.c_void_p * len(arrs))(*[_ptr(a) for a in arrs])
+
+
+def _as_u16(a: np.ndarray) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    assert a.dtype == np.uint16, "bf16 data travels as uint16 bit patterns"
+    return a
+
+
+# ---------------------------------------------------------------------------------------------
+def bf16_to_f32(bits: int) -> float:
+    return float(lib().oracle_bf16_to_f32(bits))
+
+
+def f32_to_bf16_rne(x: float) -> int:
+    return int(lib().oracle_f32_to_bf16_rne(x))
+
+
+def tgather(shards, dst: np.ndarray, D0: int, D1: int, D2: int, H: int, W: int,
+            dst_rows: int | None = None) -> np.ndarray:
+    """TGATHER closed form (TGATHER deep dive, section 二 数学语义) into ``dst`` in place."""
+    shards = [np.ascontiguousarray(s) for s in shards]
+    esz = dst.itemsize
+    for s in shards:
+        assert s.itemsize == esz and s.size == D0 * D1 * D2 * H * W
+    if dst_rows is None:
+        dst_rows = len(shards) * H
+    assert dst.flags.c_contiguous and dst.size == D0 * D1 * D2 * dst_rows * W
+    ptrs = _ptr_array(shards)
+    rc = lib().oracle_tgather(ctypes.cast(ptrs, _vp), len(shards), _ptr(dst), D0, D1, D2, H, W,
+                              dst_rows, esz)
+    if rc != 0:
+        raise ValueError("oracle_tgather rejected its arguments (rc=%d)" % rc)
+    return dst
+
+
+def gemm_f32(A: np.ndarray, B: np.ndarray) -> np.ndarray:
+    """C = A @ B^T, fp32 accumulation in ascending k (A (M,K), B (Nc,K) as bf16 bits)."""
+    A, B = _as_u16(A), _as_u16(B)
+    M, K = A.shape
+    Nc, K2 = B.shape
+    assert K == K2
+    C = np.empty((M, Nc), dtype=np.float32)
+    lib().oracle_gemm_f32(_ptr(A), _ptr(B), M, Nc, K, _ptr(C))
+    return C
+
+
+def ag_gemm(shards, B: np.ndarray):
+    """Gather the shards, then GEMM.  Returns (A (M,K) bf16 bits, C (M,Nc) fp32)."""
+    shards = [_as_u16(s) for s in shards]
+    B = _as_u16(B)
+    H, K = shards[0].shape
+    M = H * len(shards)
+    Nc = B.shape[0]
+    A = np.empty((M, K), dtype=np.uint16)
+    C = np.empty((M, Nc), dtype=np.float32)
+    ptrs = _ptr_array(shards)
+    rc = lib().oracle_ag_gemm(ctypes.cast(ptrs, _vp), len(shards), M, K, _ptr(B), Nc, _ptr(A),
+                              _ptr(C))
+    if rc != 0:
+        raise ValueError("oracle_ag_gemm rc=%d" % rc)
+    return A, C
+
+
+def ag_gemm_at(shards, B: np.ndarray, ms, ns) -> np.ndarray:
+    """Elements C[ms[i], ns[i]] of gather(shards) @ B^T, fp32 ascending-k accumulation."""
+    shards = [_as_u16(s) for s in shards]
+    B = _as_u16(B)
+    H, K = shards[0].shape
+    M = H * len(shards)
+    Nc = B.shape[0]
+    ms = np.ascontiguousarray(ms, dtype=np.int64)
+    ns = np.ascontiguousarray(ns, dtype=np.int64)
+    out = np.empty(ms.shape[0], dtype=np.float32)
+    ptrs = _ptr_array(shards)
+    rc = lib().oracle_ag_gemm_at(ctypes.cast(ptrs, _vp), len(shards), M, K, _ptr(B), Nc, _ptr(ms),
+                                 _ptr(ns), ms.shape[0], _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_ag_gemm_at rc=%d" % rc)
+    return out
+
+
+def chunk_of_row(row: int, H: int, cb: int) -> int:
+    return int(lib().oracle_chunk_of_row(row, H, cb))
+
+
+def chunks_overlapping(m0: int, m1: int, H: int, cb: int) -> list[int]:
+    cap = max(1, m1 - m0 + 1)
+    out = np.zeros(cap, dtype=np.int64)
+    n = int(lib().oracle_chunks_overlapping(m0, m1, H, cb, _ptr(out), cap))
+    return [int(x) for x in out[:n]]
+
+
+def grouped_tile(t: int, num_pid_m: int, num_pid_n: int, group_m: int) -> tuple[int, int]:
+    pm = ctypes.c_int64()
+    pn = ctypes.c_int64()
+    lib().oracle_grouped_tile(t, num_pid_m, num_pid_n, group_m, ctypes.byref(pm),
+                              ctypes.byref(pn))
+    return int(pm.value), int(pn.value)
+
+
+def ag_gemm_pivoted(shards, B: np.ndarray, cb: int, BM: int, BN: int, group_m: int,
+                    local_rank: int):
+    """Fused-schedule simulation.  Returns (rc, A_prime, C, stats dict)."""
+    shards = [_as_u16(s) for s in shards]
+    B = _as_u16(B)
+    H, K = shards[0].shape
+    M = H * len(shards)
+    Nc = B.shape[0]
+    A = np.empty((M, K), dtype=np.uint16)
+    C = np.empty((M, Nc), dtype=np.float32)
+    stats = np.zeros(6, dtype=np.int64)
+    ptrs = _ptr_array(shards)
+    rc = lib().oracle_ag_gemm_pivoted(ctypes.cast(ptrs, _vp), len(shards), M, K, _ptr(B), Nc, cb,
+                                      BM, BN, group_m, local_rank, _ptr(A), _ptr(C), _ptr(stats))
+    keys = ("waited_tiles", "flag_checks", "local_tiles", "first_pid_m",
+            "tiles_before_first_remote", "published_before_drain")
+    return rc, A, C, {k: int(v) for k, v in zip(keys, stats)}
