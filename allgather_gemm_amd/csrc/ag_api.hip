@@ -1,0 +1,373 @@
+// ag_api.hip -- host runtime behind the C ABI declared in include/aggemm.h: validation,
+// per-device workspace, epochs of the progress flags, stream ordering, and launches.
+#include "../../include/aggemm.h"
+#include "ag_internal.hpp"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+namespace ag {
+namespace {
+
+struct Workspace {
+    void* a_agg = nullptr;       // aggregate A (M, K) bf16
+    size_t a_bytes = 0;
+    uint32_t* flags = nullptr;   // progress flags, one per chunk
+    uint32_t* done = nullptr;    // finished pieces per chunk
+    int64_t nflags = 0;
+    uint32_t* ctl = nullptr;     // [0] piece ticket, [1] exit count, [4..7] status word
+    uint32_t epoch = 0;          // value of a raised flag in the last call
+    hipEvent_t last = nullptr;   // completion of the last call that used this workspace
+    bool used = false;
+};
+
+std::mutex g_mu;
+std::vector<Workspace> g_ws;
+thread_local std::string t_err;
+
+int hip_fail(hipError_t e, const char* what)
+{
+    t_err = std::string(what) + ": " + hipGetErrorString(e);
+    return AG_EHIP;
+}
+
+#define AG_HIP(call, what)                     \
+    do {                                       \
+        hipError_t e_ = (call);                \
+        if (e_ != hipSuccess)                  \
+            return hip_fail(e_, what);         \
+    } while (0)
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int current_ws(Workspace** out)
+{
+    int dev = 0;
+    AG_HIP(hipGetDevice(&dev), "hipGetDevice");
+    if (dev < 0)
+        return AG_EINVAL;
+    if ((size_t)dev >= g_ws.size())
+        g_ws.resize(dev + 1);
+    Workspace& w = g_ws[dev];
+    if (!w.ctl) {
+        AG_HIP(hipMalloc(&w.ctl, 8 * sizeof(uint32_t)), "hipMalloc(control)");
+        AG_HIP(hipMemset(w.ctl, 0, 8 * sizeof(uint32_t)), "hipMemset(control)");
+        AG_HIP(hipEventCreateWithFlags(&w.last, hipEventDisableTiming), "hipEventCreate");
+    }
+    *out = &w;
+    return AG_OK;
+}
+
+// Grows are rare; they wait for the device so no in-flight kernel still uses the old buffers.
+int ensure_flags(Workspace& w, int64_t n)
+{
+    if (n <= w.nflags)
+        return AG_OK;
+    AG_HIP(hipDeviceSynchronize(), "hipDeviceSynchronize(grow flags)");
+    if (w.flags)
+        AG_HIP(hipFree(w.flags), "hipFree(flags)");
+    if (w.done)
+        AG_HIP(hipFree(w.done), "hipFree(done)");
+    w.flags = w.done = nullptr;
+    w.nflags = 0;
+    const int64_t cap = n < 1024 ? 1024 : n;
+    if (hipMalloc(&w.flags, cap * sizeof(uint32_t)) != hipSuccess ||
+        hipMalloc(&w.done, cap * sizeof(uint32_t)) != hipSuccess)
+        return AG_ENOMEM;
+    AG_HIP(hipMemset(w.flags, 0, cap * sizeof(uint32_t)), "hipMemset(flags)");
+    AG_HIP(hipMemset(w.done, 0, cap * sizeof(uint32_t)), "hipMemset(done)");
+    w.nflags = cap;
+    w.epoch = 0;   // fresh flags are all 0, so any epoch >= 1 is new
+    return AG_OK;
+}
+
+int ensure_a(Workspace& w, size_t bytes)
+{
+    if (bytes <= w.a_bytes)
+        return AG_OK;
+    AG_HIP(hipDeviceSynchronize(), "hipDeviceSynchronize(grow A)");
+    if (w.a_agg)
+        AG_HIP(hipFree(w.a_agg), "hipFree(A)");
+    w.a_agg = nullptr;
+    w.a_bytes = 0;
+    if (hipMalloc(&w.a_agg, bytes) != hipSuccess)
+        return AG_ENOMEM;
+    w.a_bytes = bytes;
+    return AG_OK;
+}
+
+// Next flag value; on wrap-around the flags are cleared so an old value cannot match.
+int next_epoch(Workspace& w, hipStream_t s)
+{
+    if (++w.epoch == 0) {
+        AG_HIP(launch_fill_u32(w.flags, w.nflags, 0u, s), "fill flags");
+        w.epoch = 1;
+    }
+    return AG_OK;
+}
+
+int begin_use(Workspace& w, hipStream_t s)
+{
+    if (w.used)
+        AG_HIP(hipStreamWaitEvent(s, w.last, 0), "hipStreamWaitEvent");
+    return AG_OK;
+}
+
+int end_use(Workspace& w, hipStream_t s)
+{
+    AG_HIP(hipEventRecord(w.last, s), "hipEventRecord");
+    w.used = true;
+    return AG_OK;
+}
+
+int validate_gemm(const void* const* shards, int32_t N, int64_t M, int64_t K, const void* B,
+                  int64_t Nc, void* C, int64_t cb, const ag_options* opt)
+{
+    if (!shards || N < 1 || N > kMaxShards || M < 0 || K < 0 || Nc < 0 || cb < 1)
+        return AG_EINVAL;
+    if (M % N != 0 || K % 8 != 0)
+        return AG_EINVAL;
+    if (K > (int64_t(1) << 21))
+        return AG_EUNSUPPORTED;
+    if (opt) {
+        if (opt->mode < AG_MODE_FUSED || opt->mode > AG_MODE_GEMM_ONLY || opt->local_rank < 0 ||
+            opt->local_rank >= N || opt->skip_producer < 0 || opt->skip_producer > 1)
+            return AG_EINVAL;
+        if (opt->mode == AG_MODE_GEMM_ONLY && !opt->a_out)
+            return AG_EINVAL;
+        if (opt->a_out && !aligned16(opt->a_out))
+            return AG_EINVAL;
+    }
+    if (M == 0 || Nc == 0)
+        return AG_OK;
+    if (!C || !aligned16(C))
+        return AG_EINVAL;
+    if (K > 0) {   // with K == 0 nothing is read, so empty inputs may have null pointers
+        if (!B || !aligned16(B))
+            return AG_EINVAL;
+        for (int r = 0; r < N; ++r)
+            if (!shards[r] || !aligned16(shards[r]))
+                return AG_EINVAL;
+    }
+    const int64_t H = M / N;
+    const int64_t chunks = (int64_t)N * ((H + cb - 1) / cb);
+    if (chunks > (int64_t(1) << 30))
+        return AG_EUNSUPPORTED;
+    return AG_OK;
+}
+
+}  // namespace
+}  // namespace ag
+
+using namespace ag;
+
+extern "C" int ag_gemm_ex(const void* const* shards, int32_t N, int64_t M, int64_t K, const void* B,
+                          int64_t Nc, void* C, int64_t comm_block_rows, void* stream,
+                          const ag_options* opt)
+{
+    int rc = validate_gemm(shards, N, M, K, B, Nc, C, comm_block_rows, opt);
+    if (rc != AG_OK || M == 0 || Nc == 0)
+        return rc;
+    const int mode = opt ? opt->mode : AG_MODE_FUSED;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    std::lock_guard<std::mutex> lock(g_mu);
+    Workspace* w = nullptr;
+    if ((rc = current_ws(&w)) != AG_OK)
+        return rc;
+    const int64_t H = M / N;
+    const int64_t S = (H + comm_block_rows - 1) / comm_block_rows;
+    const int64_t nchunks = (int64_t)N * S;
+    void* a_buf = opt ? opt->a_out : nullptr;
+    if (!a_buf && K > 0) {
+        if ((rc = ensure_a(*w, (size_t)M * K * 2)) != AG_OK)
+            return rc;
+        a_buf = w->a_agg;
+    }
+    if ((rc = ensure_flags(*w, nchunks)) != AG_OK)
+        return rc;
+    if ((rc = begin_use(*w, s)) != AG_OK)
+        return rc;
+
+    GemmArgs g;
+    std::memset(&g, 0, sizeof g);
+    g.A = a_buf;
+    g.B = B;
+    g.C = C;
+    g.M = M;
+    g.Nc = Nc;
+    g.K = K;
+    for (int r = 0; r < N; ++r)
+        g.shards[r] = shards[r];
+    g.nshards = N;
+    g.local_rank = opt ? opt->local_rank : 0;
+    g.H = H;
+    g.cb = comm_block_rows;
+    g.flags = w->flags;
+    g.done = w->done;
+    g.ticket = w->ctl;
+    g.status = w->ctl + 4;
+    const int64_t timeout_us = (opt && opt->timeout_us > 0) ? opt->timeout_us : 10000000;
+    g.spin_limit = timeout_us * 100;   // s_memrealtime runs at 100 MHz
+    g.reverse_order = opt ? opt->reverse_order : 0;
+
+    if (K == 0) {
+        // empty reduction: C = 0, nothing to gather
+        AG_HIP(launch_gemm(g, kGemmPlain, s), "launch gemm");
+        return end_use(*w, s);
+    }
+    if (mode == AG_MODE_UNFUSED) {
+        GatherDesc d;
+        std::memset(&d, 0, sizeof d);
+        for (int r = 0; r < N; ++r)
+            d.src[r] = shards[r];
+        d.dst = a_buf;
+        d.nranks = N;
+        d.elem_size = 2;
+        d.planes = 1;
+        d.H = H;
+        d.W = K;
+        d.dst_rows = M;
+        d.valid_rows = H;
+        d.valid_cols = K;
+        AG_HIP(launch_tgather(d, s), "launch tgather");
+        AG_HIP(launch_gemm(g, kGemmPlain, s), "launch gemm");
+    } else {
+        if ((rc = next_epoch(*w, s)) != AG_OK)
+            return rc;
+        g.epoch = w->epoch;
+        if (mode == AG_MODE_GEMM_ONLY) {
+            AG_HIP(launch_fill_u32(w->flags, nchunks, g.epoch, s), "fill flags");
+            g.copy_pieces = 0;
+        } else {
+            g.copy_pieces = (opt && opt->skip_producer) ? 0 : 1;
+        }
+        AG_HIP(launch_gemm(g, kGemmFused, s), "launch fused gemm");
+    }
+    return end_use(*w, s);
+}
+
+extern "C" int ag_gemm(const void* const* shards, int32_t N, int64_t M, int64_t K, const void* B,
+                       int64_t Nc, void* C, int64_t comm_block_rows, void* stream)
+{
+    return ag_gemm_ex(shards, N, M, K, B, Nc, C, comm_block_rows, stream, nullptr);
+}
+
+extern "C" int ag_gemm_unfused(const void* const* shards, int32_t N, int64_t M, int64_t K,
+                               const void* B, int64_t Nc, void* C, int64_t comm_block_rows,
+                               void* stream)
+{
+    ag_options o;
+    std::memset(&o, 0, sizeof o);
+    o.mode = AG_MODE_UNFUSED;
+    return ag_gemm_ex(shards, N, M, K, B, Nc, C, comm_block_rows, stream, &o);
+}
+
+extern "C" int tgather_ex(const void* const* shards, int32_t N, void* dst, int64_t D0, int64_t D1,
+                          int64_t D2, int64_t H, int64_t W, int64_t dst_rows, int64_t valid_rows,
+                          int64_t valid_cols, int32_t elem_size, void* stream)
+{
+    if (!shards || N < 1 || N > kMaxShards || D0 < 0 || D1 < 0 || D2 < 0 || H < 0 || W < 0)
+        return AG_EINVAL;
+    if (valid_rows < 1 || valid_cols < 1)
+        return AG_EINVAL;
+    if (!(elem_size == 1 || elem_size == 2 || elem_size == 4 || elem_size == 8))
+        return AG_EINVAL;
+    if (dst_rows < (int64_t)N * H)
+        return AG_EINVAL;
+    if (D0 == 0 || D1 == 0 || D2 == 0 || H == 0 || W == 0)
+        return AG_OK;                                   // nothing moves
+    if (!dst)
+        return AG_EINVAL;
+    for (int r = 0; r < N; ++r)
+        if (!shards[r])
+            return AG_EINVAL;
+    GatherDesc d;
+    std::memset(&d, 0, sizeof d);
+    for (int r = 0; r < N; ++r)
+        d.src[r] = shards[r];
+    d.dst = dst;
+    d.nranks = N;
+    d.elem_size = elem_size;
+    d.planes = D0 * D1 * D2;
+    d.H = H;
+    d.W = W;
+    d.dst_rows = dst_rows;
+    d.valid_rows = valid_rows;
+    d.valid_cols = valid_cols;
+    AG_HIP(launch_tgather(d, static_cast<hipStream_t>(stream)), "launch tgather");
+    return AG_OK;
+}
+
+extern "C" int tgather(const void* const* shards, int32_t N, void* dst, int64_t D0, int64_t D1,
+                       int64_t D2, int64_t H, int64_t W, int64_t valid_rows, int64_t valid_cols,
+                       int32_t elem_size, void* stream)
+{
+    return tgather_ex(shards, N, dst, D0, D1, D2, H, W, (int64_t)N * H, valid_rows, valid_cols,
+                      elem_size, stream);
+}
+
+extern "C" int ag_check(void* stream, int64_t info[4])
+{
+    std::lock_guard<std::mutex> lock(g_mu);
+    Workspace* w = nullptr;
+    int rc = current_ws(&w);
+    if (rc != AG_OK)
+        return rc;
+    AG_HIP(hipStreamSynchronize(static_cast<hipStream_t>(stream)), "hipStreamSynchronize");
+    uint32_t st[4] = {0, 0, 0, 0};
+    AG_HIP(hipMemcpy(st, w->ctl + 4, sizeof st, hipMemcpyDeviceToHost), "hipMemcpy(status)");
+    if (info)
+        for (int i = 0; i < 4; ++i)
+            info[i] = st[i];
+    if (st[0] == 0)
+        return AG_OK;
+    AG_HIP(hipMemset(w->ctl + 4, 0, 4 * sizeof(uint32_t)), "hipMemset(status)");
+    // a wait that gave up leaves piece counters of that call in an unknown state
+    AG_HIP(hipMemset(w->ctl, 0, 2 * sizeof(uint32_t)), "hipMemset(ticket)");
+    if (w->done)
+        AG_HIP(hipMemset(w->done, 0, w->nflags * sizeof(uint32_t)), "hipMemset(done)");
+    return AG_ETIMEOUT;
+}
+
+extern "C" const char* ag_status_str(int status)
+{
+    switch (status) {
+    case AG_OK: return "ok";
+    case AG_EINVAL: return "invalid argument";
+    case AG_ENOMEM: return "out of device memory";
+    case AG_EHIP: return "HIP runtime error";
+    case AG_ETIMEOUT: return "timed out waiting on a chunk flag";
+    case AG_EUNSUPPORTED: return "unsupported shape";
+    default: return "unknown status";
+    }
+}
+
+extern "C" const char* ag_last_error(void) { return t_err.c_str(); }
+
+extern "C" void ag_finalize(void)
+{
+    std::lock_guard<std::mutex> lock(g_mu);
+    int prev = 0;
+    if (hipGetDevice(&prev) != hipSuccess)
+        return;
+    for (size_t dev = 0; dev < g_ws.size(); ++dev) {
+        Workspace& w = g_ws[dev];
+        if (!w.ctl)
+            continue;
+        if (hipSetDevice((int)dev) != hipSuccess)
+            continue;
+        (void)hipDeviceSynchronize();
+        (void)hipFree(w.a_agg);
+        (void)hipFree(w.flags);
+        (void)hipFree(w.done);
+        (void)hipFree(w.ctl);
+        (void)hipEventDestroy(w.last);
+        w = Workspace();
+    }
+    (void)hipSetDevice(prev);
+}

@@ -1,0 +1,88 @@
+// ag_device.hpp -- device-side building blocks shared by the gfx950 kernels of libaggemm:
+// bf16 vector types, buffer resources for LDS-DMA loads, and the chunk-flag protocol.
+//
+// Flag protocol (fused AllGather + MatMul article, "数据搬运与细粒度同步" and
+// "wait_signal 的实现与语义"): a chunk's rows must be visible before its flag says so.  The
+// producer side drains its stores, then publishes with an agent-scope release; the consumer
+// polls with relaxed agent-scope loads and, once it sees the value it waits for, issues an
+// agent-scope acquire fence before any of its waves reads the chunk.  Agent scope is what
+// makes the data visible across the eight XCDs (separate L2s) of one MI355X.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ag {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Buffer resource word 3 for gfx9-family parts (raw buffer, 32-bit dword format).
+constexpr int kRsrcWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes,
+                                             kRsrcWord3);
+}
+
+// 16 bytes from global memory (rsrc + voffset) straight into LDS: lane l of the wave writes
+// bytes [16 l, 16 l + 16) after the wave-uniform LDS address `lds_wave_base`.  An offset at or
+// beyond the resource's size yields zeros.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, void* lds_wave_base, uint32_t voffset)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)lds_wave_base, 16, (int)voffset, 0, 0, 0);
+}
+
+// A value every lane of the workgroup holds (one lane wrote it to LDS before a barrier), made
+// wave-uniform for the compiler.  Loop exits and branches around barriers must depend only on
+// such values: a condition the compiler believes divergent gets structurized per lane, and a
+// one-lane region inside a loop with barriers can then be moved out of the loop while the other
+// lanes keep iterating.
+__device__ __forceinline__ int64_t uniform_i64(int64_t v)
+{
+    const uint64_t u = (uint64_t)v;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// s_waitcnt encodings (gfx9): vmcnt in [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
+__device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0x0000); }
+
+// ----------------------------------------------------------------------------------- flags
+// Every access to a word that another workgroup writes is a read-modify-write atomic: the eight
+// XCDs have separate L2s, and an RMW is resolved at the device's point of coherence, so a poll
+// can never keep returning a copy cached in the polling XCD's L2.
+__device__ __forceinline__ uint32_t flag_peek(uint32_t* f)
+{
+    return __hip_atomic_fetch_add(f, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void flag_publish(uint32_t* f, uint32_t value)
+{
+    (void)__hip_atomic_exchange(f, value, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
+// Status word: the first failure wins (0 = clean).  Layout: [code, chunk, tile, 0].  Called by
+// all 64 lanes of one wave: lane 0 contributes the code, the others OR in zero, and the
+// follow-up writes repeat one value, so there is no one-lane branch.
+__device__ __forceinline__ void report_failure(uint32_t* status, uint32_t code, uint32_t chunk, uint32_t tile)
+{
+    const uint32_t mine = (threadIdx.x & 63) == 0 ? code : 0u;
+    const uint32_t prev = __builtin_amdgcn_readfirstlane(
+        __hip_atomic_fetch_or(&status[0], mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    if (prev == 0) {
+        (void)__hip_atomic_exchange(&status[1], chunk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        (void)__hip_atomic_exchange(&status[2], tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+}  // namespace ag

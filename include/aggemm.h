@@ -1,0 +1,126 @@
+/*
+ * aggemm.h -- C ABI of libaggemm: chunked AllGather fused with a bf16 GEMM, and TGATHER, on one
+ * AMD Instinct MI355X (gfx950).
+ *
+ * Pages this library implements:
+ *   [AGMM]  "Triton第四课：基于对称内存融合 AllGather 与 MatMul，提速1.56倍" (the fused
+ *           AllGather + MatMul pipeline: comm blocks, progress flags, rotated tile order)
+ *   [TGATH] "CANN PTO-ISA TGATHER 指令深度解析：跨 Rank 行拼接 Gather 的实现原理与开发指南"
+ *           (the root-side row-concatenating gather with 2D sliding tiles)
+ *
+ * On one GPU the N "ranks" are N separate device buffers ("shards"); the AllGather is an
+ * HBM-to-HBM copy of their rows into one aggregate buffer.
+ *
+ * Conventions for every entry point:
+ *   - All tensors are caller-owned DEVICE memory on the current HIP device, row-major and
+ *     contiguous.  `shards` itself is a HOST array of N device pointers, read during the call only.
+ *   - bf16 is IEEE binary32 truncated to its upper 16 bits (the layout of torch.bfloat16).
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls are enqueued on it and return
+ *     before the GPU work finishes; results are valid once the stream has reached that point.
+ *   - Arguments are validated before anything is enqueued; on a negative return nothing was
+ *     enqueued.  Outputs must not overlap inputs.
+ *   - The library keeps a per-device workspace (aggregate A buffer, progress flags, counters, a
+ *     status word) that grows on demand and is released by ag_finalize().  Calls that use it are
+ *     ordered with one another through an event, so at most one AG-GEMM uses it at a time.
+ */
+#ifndef AGGEMM_H
+#define AGGEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+#define AG_OK            0
+#define AG_EINVAL       -1   /* an argument was rejected; nothing was enqueued */
+#define AG_ENOMEM       -2   /* the workspace could not grow */
+#define AG_EHIP         -3   /* the HIP runtime reported an error (message: ag_last_error()) */
+#define AG_ETIMEOUT     -4   /* (ag_check) a tile gave up waiting on a chunk flag */
+#define AG_EUNSUPPORTED -5   /* shape outside the library's limits (see each entry point) */
+
+/* Schedules of ag_gemm_ex. */
+#define AG_MODE_FUSED      0  /* chunked copy and GEMM in one persistent grid, per-chunk flags */
+#define AG_MODE_UNFUSED    1  /* full gather (tgather kernel), then the GEMM: the serial schedule */
+#define AG_MODE_GEMM_ONLY  2  /* the fused GEMM with every flag already raised and no copy */
+
+typedef struct ag_options {
+    int32_t mode;          /* AG_MODE_* */
+    int32_t local_rank;    /* shard whose rows the rotated tile walk starts at, 0..N-1 */
+    void *a_out;           /* NULL, or an (M, K) bf16 device buffer that receives the gathered A.
+                              Required for AG_MODE_GEMM_ONLY, where it must already hold it. */
+    int64_t timeout_us;    /* give-up time of one flag wait, microseconds (<= 0: 10 s) */
+    int32_t reverse_order; /* test aid: the copy claims chunks in reverse ready order */
+    int32_t skip_producer; /* test aid (AG_MODE_FUSED): copy nothing and leave the flags stale, so
+                              every non-local tile's wait ends through timeout_us; ag_check then
+                              reports AG_ETIMEOUT.  C is meaningless after such a call. */
+} ag_options;
+
+/*
+ * C = gather(shards) * B^T with the fused schedule ([AGMM] 融合后的流水线, MatMul 按需等待).
+ *   shards[r]        (H, K) bf16, H = M / N; shard r holds rows [r*H, (r+1)*H) of A
+ *   N                number of shards, 1..64
+ *   M, K             rows of the gathered A and the reduction length; M % N == 0, K % 8 == 0,
+ *                    K <= 2^21
+ *   B                (Nc, K) bf16 (the weight stored row-major by output column)
+ *   C                (M, Nc) bf16 output, written with round-to-nearest-even from fp32 sums
+ *   comm_block_rows  rows per comm block (chunk) inside each shard, >= 1; the last chunk of a
+ *                    shard may be shorter.  Chunk r*S + s (S = ceil(H / comm_block_rows)) has
+ *                    its own uint32 progress flag ([AGMM] 数据搬运与细粒度同步).
+ * Device pointers must be 16-byte aligned.  M == 0 or Nc == 0 enqueues nothing; K == 0 writes
+ * zeros (shards and B may then be NULL).  The local shard is shard 0 (ag_gemm_ex chooses
+ * another).
+ */
+int ag_gemm(const void *const *shards, int32_t N, int64_t M, int64_t K, const void *B,
+            int64_t Nc, void *C, int64_t comm_block_rows, void *stream);
+
+/* Same arguments; the serial schedule ([AGMM] 为什么要融合 AllGather 与 MatMul): the whole
+ * gather into the workspace first, then the GEMM.  Bitwise equal to ag_gemm's C. */
+int ag_gemm_unfused(const void *const *shards, int32_t N, int64_t M, int64_t K, const void *B,
+                    int64_t Nc, void *C, int64_t comm_block_rows, void *stream);
+
+/* ag_gemm with options (NULL = defaults: fused, local_rank 0, internal buffer, 10 s). */
+int ag_gemm_ex(const void *const *shards, int32_t N, int64_t M, int64_t K, const void *B,
+               int64_t Nc, void *C, int64_t comm_block_rows, void *stream,
+               const ag_options *opt);
+
+/*
+ * TGATHER ([TGATH] 二 数学语义): dst[d0,d1,d2, r*H + i, j] = shards[r][d0,d1,d2, i, j].
+ *   shards[r]            (D0, D1, D2, H, W) tensor of elem_size-byte elements, r < N (1..64)
+ *   dst                  (D0, D1, D2, N*H, W) tensor
+ *   valid_rows/cols      extent of the staging tile that slides over each rank's (H, W) plane
+ *                        ([TGATH] 6.1, 7.4): >= 1; the last row / column tile is ragged when they
+ *                        do not divide H / W; values above H / W mean one tile spans the plane.
+ *                        The result does not depend on them (a copy is exact); the work split does.
+ *   elem_size            1, 2, 4 or 8 bytes.
+ * Any extent of 0 enqueues nothing ([TGATH] 7.4).  16-byte aligned pointers with
+ * W * elem_size % 16 == 0 take the LDS-staged 16-byte path; anything else a slower element path.
+ */
+int tgather(const void *const *shards, int32_t N, void *dst, int64_t D0, int64_t D1, int64_t D2,
+            int64_t H, int64_t W, int64_t valid_rows, int64_t valid_cols, int32_t elem_size,
+            void *stream);
+
+/* tgather into a taller dst of shape (D0, D1, D2, dst_rows, W), dst_rows >= N*H; rows at or
+ * beyond N*H of every plane are left untouched ([TGATH] 7.2 内存约束). */
+int tgather_ex(const void *const *shards, int32_t N, void *dst, int64_t D0, int64_t D1,
+               int64_t D2, int64_t H, int64_t W, int64_t dst_rows, int64_t valid_rows,
+               int64_t valid_cols, int32_t elem_size, void *stream);
+
+/* Waits for `stream`, then reads and clears the current device's status word.  Returns AG_OK,
+ * or AG_ETIMEOUT with info = {code, chunk, tile, 0} for the first flag wait that gave up. */
+int ag_check(void *stream, int64_t info[4]);
+
+/* Static text for a return code. */
+const char *ag_status_str(int status);
+
+/* Text of the last HIP error seen by the library on this thread's calls ("" if none). */
+const char *ag_last_error(void);
+
+/* Waits for all devices the library used and frees every workspace.  Safe to call repeatedly. */
+void ag_finalize(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* AGGEMM_H */
