@@ -20,10 +20,12 @@ struct Workspace {
     uint32_t* flags = nullptr;   // progress flags, one per chunk
     uint32_t* done = nullptr;    // finished pieces per chunk
     int64_t nflags = 0;
-    uint32_t* ctl = nullptr;     // [0] piece ticket, [1] exit count, [4..7] status word
+    uint32_t* ctl = nullptr;     // [0] piece counter, [4..7] status word
     uint32_t epoch = 0;          // value of a raised flag in the last call
     hipEvent_t last = nullptr;   // completion of the last call that used this workspace
     bool used = false;
+    hipStream_t side = nullptr;  // the fused schedule's copy stream (default priority)
+    hipEvent_t fork = nullptr, join = nullptr;
 };
 
 std::mutex g_mu;
@@ -58,6 +60,9 @@ int current_ws(Workspace** out)
         AG_HIP(hipMalloc(&w.ctl, 8 * sizeof(uint32_t)), "hipMalloc(control)");
         AG_HIP(hipMemset(w.ctl, 0, 8 * sizeof(uint32_t)), "hipMemset(control)");
         AG_HIP(hipEventCreateWithFlags(&w.last, hipEventDisableTiming), "hipEventCreate");
+        AG_HIP(hipEventCreateWithFlags(&w.fork, hipEventDisableTiming), "hipEventCreate");
+        AG_HIP(hipEventCreateWithFlags(&w.join, hipEventDisableTiming), "hipEventCreate");
+        AG_HIP(hipStreamCreateWithFlags(&w.side, hipStreamNonBlocking), "hipStreamCreate");
     }
     *out = &w;
     return AG_OK;
@@ -243,10 +248,22 @@ extern "C" int ag_gemm_ex(const void* const* shards, int32_t N, int64_t M, int64
         if (mode == AG_MODE_GEMM_ONLY) {
             AG_HIP(launch_fill_u32(w->flags, nchunks, g.epoch, s), "fill flags");
             g.copy_pieces = 0;
+            AG_HIP(launch_gemm(g, kGemmFused, s), "launch fused gemm");
+        } else if (opt && opt->skip_producer) {
+            g.copy_pieces = 0;
+            AG_HIP(launch_gemm(g, kGemmFused, s), "launch fused gemm");
         } else {
-            g.copy_pieces = (opt && opt->skip_producer) ? 0 : 1;
+            // Producer on the side stream, GEMM on the caller's; both claim pieces from one
+            // counter, reset first.  The call ends when both have.
+            g.copy_pieces = 1;
+            AG_HIP(launch_fill_u32(w->ctl, 1, 0u, s), "reset piece counter");
+            AG_HIP(hipEventRecord(w->fork, s), "hipEventRecord(fork)");
+            AG_HIP(hipStreamWaitEvent(w->side, w->fork, 0), "hipStreamWaitEvent(side)");
+            AG_HIP(launch_producer(g, w->side), "launch producer");
+            AG_HIP(launch_gemm(g, kGemmFused, s), "launch fused gemm");
+            AG_HIP(hipEventRecord(w->join, w->side), "hipEventRecord(join)");
+            AG_HIP(hipStreamWaitEvent(s, w->join, 0), "hipStreamWaitEvent(join)");
         }
-        AG_HIP(launch_gemm(g, kGemmFused, s), "launch fused gemm");
     }
     return end_use(*w, s);
 }
@@ -367,6 +384,9 @@ extern "C" void ag_finalize(void)
         (void)hipFree(w.done);
         (void)hipFree(w.ctl);
         (void)hipEventDestroy(w.last);
+        (void)hipEventDestroy(w.fork);
+        (void)hipEventDestroy(w.join);
+        (void)hipStreamDestroy(w.side);
         w = Workspace();
     }
     (void)hipSetDevice(prev);

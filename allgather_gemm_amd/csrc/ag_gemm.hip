@@ -9,10 +9,12 @@
 //    reads the aggregate A buffer;
 //  * section 数据搬运与细粒度同步: a chunk's flag is raised only after its rows have landed;
 //  * section wait_signal 的实现与语义: one lane polls, then a workgroup barrier releases the block.
-// The producer is not a separate stream here: the chunk copies are split into pieces that the
-// workgroups of this same grid claim from a counter whenever they would otherwise wait (and
-// after their last tile), so every claimed piece is held by a running workgroup and no wait can
-// deadlock, whatever the residency of the grid.
+// The producer runs on a second stream (section 融合后的流水线 has the copy on a backend stream
+// beside the MatMul): a small copy kernel whose workgroups sit next to the GEMM's on every CU.
+// The chunk copies are split into pieces claimed from one counter, in ready order, by the
+// producer's workgroups and also by any GEMM workgroup that would otherwise wait.  A piece is
+// claimed only by a running workgroup, so no wait can deadlock whatever the two grids' residency
+// or launch order: a GEMM that starts alone copies what it needs itself.
 //
 // Tiling (gfx950): 256x256 output tile per 256-thread workgroup (4 waves, 2x2, 128x128 each),
 // K step 64, v_mfma_f32_32x32x16_bf16, A/B tiles staged in LDS by buffer_load ... lds (16 B per
@@ -457,17 +459,19 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(KParams p)
         __syncthreads();   // LDS is free again for the next tile's loads
     }
 
-    if (MODE == kGemmFused && a.copy_pieces) {
-        drain_pieces(p, tid, wave0, &s_cmd, exhausted);
-        if (wave0) {
-            const uint32_t done_wgs = uniform_u32(__hip_atomic_fetch_add(
-                &a.ticket[1], lane0_one(), __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT)) + 1;
-            if (done_wgs == (uint32_t)G) {   // last workgroup out resets the counters
-                (void)__hip_atomic_exchange(&a.ticket[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                (void)__hip_atomic_exchange(&a.ticket[1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
-    }
+}
+
+// Producer of the fused schedule, on its own stream: claims pieces in ready order from the same
+// counter the GEMM's waiting workgroups use, copies them and raises the chunk flags.  It never
+// waits on anything.  Small (no LDS tile, few VGPRs), so its workgroups fit beside the GEMM's on
+// every CU and the copy overlaps the MFMA work.
+__global__ __launch_bounds__(NT) void producer_kernel(KParams p)
+{
+    __shared__ int64_t s_cmd;
+    const int tid = threadIdx.x;
+    const bool wave0 = __builtin_amdgcn_readfirstlane(tid >> 6) == 0;
+    bool exhausted = false;
+    drain_pieces(p, tid, wave0, &s_cmd, exhausted);
 }
 
 __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v)
@@ -476,33 +480,11 @@ __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v)
         p[i] = v;
 }
 
-int g_num_cus = 0;
+constexpr int kMaxDevices = 64;
+int g_num_cus[kMaxDevices] = {};
 
-}  // namespace
-
-int gemm_tile_m() { return BM; }
-int gemm_tile_n() { return BN; }
-
-hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t stream)
+KParams make_params(const GemmArgs& a, GemmMode mode)
 {
-    if (n <= 0)
-        return hipSuccess;
-    const int blocks = (int)std::min<int64_t>((n + 255) / 256, 1024);
-    fill_u32_kernel<<<blocks, 256, 0, stream>>>(p, n, value);
-    return hipGetLastError();
-}
-
-hipError_t launch_gemm(const GemmArgs& a, GemmMode mode, hipStream_t stream)
-{
-    if (g_num_cus == 0) {
-        int dev = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e != hipSuccess)
-            return e;
-        e = hipDeviceGetAttribute(&g_num_cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess)
-            return e;
-    }
     KParams p;
     p.a = a;
     p.num_pid_m = (int)((a.M + BM - 1) / BM);
@@ -523,12 +505,67 @@ hipError_t launch_gemm(const GemmArgs& a, GemmMode mode, hipStream_t stream)
         p.ppc = (a.cb + p.piece_rows - 1) / p.piece_rows;
         p.npieces = a.copy_pieces ? p.nchunks * p.ppc : 0;
     }
+    return p;
+}
+
+hipError_t num_cus(int* out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipDeviceGetAttribute(out, hipDeviceAttributeMultiprocessorCount, dev);
+    if (g_num_cus[dev] == 0) {
+        e = hipDeviceGetAttribute(&g_num_cus[dev], hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess)
+            return e;
+    }
+    *out = g_num_cus[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+int gemm_tile_m() { return BM; }
+int gemm_tile_n() { return BN; }
+
+hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t stream)
+{
+    if (n <= 0)
+        return hipSuccess;
+    const int blocks = (int)std::min<int64_t>((n + 255) / 256, 1024);
+    fill_u32_kernel<<<blocks, 256, 0, stream>>>(p, n, value);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmArgs& a, GemmMode mode, hipStream_t stream)
+{
+    int cus = 0;
+    hipError_t e = num_cus(&cus);
+    if (e != hipSuccess)
+        return e;
+    const KParams p = make_params(a, mode);
     const int64_t tiles = (int64_t)p.num_pid_m * p.num_pid_n;
-    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(tiles, g_num_cus));
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(tiles, cus));
     if (mode == kGemmFused)
         gemm_kernel<kGemmFused><<<grid, NT, 0, stream>>>(p);
     else
         gemm_kernel<kGemmPlain><<<grid, NT, 0, stream>>>(p);
+    return hipGetLastError();
+}
+
+hipError_t launch_producer(const GemmArgs& a, hipStream_t stream)
+{
+    int cus = 0;
+    hipError_t e = num_cus(&cus);
+    if (e != hipSuccess)
+        return e;
+    const KParams p = make_params(a, kGemmFused);
+    if (p.npieces <= 0)
+        return hipSuccess;
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(p.npieces, cus));
+    producer_kernel<<<grid, NT, 0, stream>>>(p);
     return hipGetLastError();
 }
 

@@ -39,7 +39,7 @@ struct GemmArgs {
     int64_t cb;             // comm block rows
     uint32_t* flags;        // progress[nshards * S]
     uint32_t* done;         // per-chunk finished-piece counters
-    uint32_t* ticket;       // piece claim counter, exit counter
+    uint32_t* ticket;       // [0] piece claim counter (shared by producer and GEMM)
     uint32_t* status;       // [code, chunk, tile, spins]
     uint32_t epoch;         // value a published flag holds during this call
     int copy_pieces;        // 1: the grid also performs the copy; 0: flags are already set
@@ -48,6 +48,10 @@ struct GemmArgs {
 };
 
 hipError_t launch_gemm(const GemmArgs& a, GemmMode mode, hipStream_t stream);
+
+// Copy kernel of the fused schedule (all pieces, ready order); launch it on a side stream next to
+// the fused GEMM.  The piece counter (ticket[0]) must be 0 when either kernel starts.
+hipError_t launch_producer(const GemmArgs& a, hipStream_t stream);
 
 // Small helper kernel: flags[0..n) = value (used for the GEMM-only schedule and epoch wrap).
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t stream);
