@@ -53,7 +53,24 @@ __device__ __forceinline__ int64_t uniform_i64(int64_t v)
 
 // s_waitcnt encodings (gfx9): vmcnt in [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
 __device__ __forceinline__ void wait_vmcnt0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// At most N vector memory operations of this wave still outstanding (N < 64).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit field");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
 __device__ __forceinline__ void wait_all() { __builtin_amdgcn_s_waitcnt(0x0000); }
+
+// Workgroup barrier after which every wave reads the LDS values any wave wrote before it.  The
+// LDS writes are drained here explicitly (lgkmcnt 0, with a compiler memory barrier) instead of
+// being left to the lowering of __syncthreads(), which was seen to drop that wait on a loop
+// back edge: a wave could then pass the barrier and read the previous value.
+__device__ __forceinline__ void barrier_after_lds_write()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __syncthreads();
+}
 
 // ----------------------------------------------------------------------------------- flags
 // Every access to a word that another workgroup writes is a read-modify-write atomic: the eight

@@ -33,7 +33,7 @@ constexpr int NT = 256;                        // threads per workgroup
 constexpr int SLOTS = BM * BK * 2 / 16;        // 16-byte slots per operand tile (2048)
 constexpr int TILE_BYTES = SLOTS * 16;         // 32 KiB per operand tile
 constexpr int GROUP_M = 8;                     // tile rows per group of the grouped order
-constexpr int64_t PIECE_BYTES = 256 * 1024;    // target bytes per producer piece
+constexpr int64_t PIECE_BYTES = 64 * 1024;     // target bytes per copy piece
 
 static_assert(BM == BN, "A and B tiles share one LDS layout");
 
@@ -103,18 +103,21 @@ __device__ __forceinline__ Piece piece_of(const KParams& p, int64_t q)
     return pc;
 }
 
-// All threads: copy piece q with 16-byte loads/stores (4 in flight per lane), drain this wave's
-// stores, then a barrier -- after it, thread 0's release covers the whole piece.
+// All threads: copy piece q with 16-byte loads/stores (8 in flight per lane), drain this wave's
+// stores, then a barrier -- after it, wave 0's release covers the whole piece.
 __device__ void copy_piece_rows(const KParams& p, int64_t q, int tid)
 {
+    constexpr int U = 8;
     const Piece pc = piece_of(p, q);
     int64_t u = tid;
-    for (; u + 3 * NT < pc.units; u += 4 * NT) {
-        i32x4 v0 = pc.src[u], v1 = pc.src[u + NT], v2 = pc.src[u + 2 * NT], v3 = pc.src[u + 3 * NT];
-        pc.dst[u] = v0;
-        pc.dst[u + NT] = v1;
-        pc.dst[u + 2 * NT] = v2;
-        pc.dst[u + 3 * NT] = v3;
+    for (; u + (U - 1) * NT < pc.units; u += U * NT) {
+        i32x4 v[U];
+#pragma unroll
+        for (int i = 0; i < U; ++i)
+            v[i] = pc.src[u + i * NT];
+#pragma unroll
+        for (int i = 0; i < U; ++i)
+            pc.dst[u + i * NT] = v[i];
     }
     for (; u < pc.units; u += NT)
         pc.dst[u] = pc.src[u];
@@ -137,8 +140,11 @@ __device__ void publish_piece(const KParams& p, int64_t q)
     const GemmArgs& a = p.a;
     const int64_t c = piece_of(p, q).chunk;
     const uint32_t old = uniform_u32(
-        __hip_atomic_fetch_add(&a.done[c], lane0_one(), __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT));
+        __hip_atomic_fetch_add(&a.done[c], lane0_one(), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT));
     if (old + 1 == (uint32_t)p.ppc) {
+        // the other pieces' releases are in this counter's release sequence: acquire them (once
+        // per chunk, not per piece) so the flag's release below covers their rows too
+        acquire_agent();
         (void)__hip_atomic_exchange(&a.done[c], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         flag_publish(&a.flags[c], a.epoch);
     }
@@ -198,7 +204,7 @@ __device__ void wait_rows(const KParams& p, int64_t m0, int64_t m1, int64_t tile
         if (wave0)
             *s_cmd = decide_wait(p, c, t_start, tile, exhausted);
         for (;;) {
-            __syncthreads();
+            barrier_after_lds_write();
             const int64_t cmd = uniform_i64(*s_cmd);
             __syncthreads();
             if (cmd == kReady)
@@ -222,14 +228,14 @@ __device__ void wait_rows(const KParams& p, int64_t m0, int64_t m1, int64_t tile
     __syncthreads();
 }
 
-// After the last tile: copy whatever no tile needed (the local shard's chunks at least), so the
-// aggregate buffer ends as the full gather.  Same loop shape as wait_rows.
-__device__ void drain_pieces(const KParams& p, int tid, bool wave0, int64_t* s_cmd, bool& exhausted)
+// Producer loop: claim, copy, publish until no piece is left.  Same loop shape as wait_rows.
+__device__ void drain_pieces(const KParams& p, int tid, bool wave0, int64_t* s_cmd)
 {
+    bool exhausted = false;
     if (wave0)
         *s_cmd = claim_next(p, exhausted);
     for (;;) {
-        __syncthreads();
+        barrier_after_lds_write();
         const int64_t q = uniform_i64(*s_cmd);
         __syncthreads();
         if (q < 0)
@@ -285,7 +291,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(KParams p)
         b_off[kk] = (wn * 128 + fr) * 128 + phys * 16;
     }
 
-    bool exhausted = false;   // (thread 0) no piece left to claim in this call
+    bool exhausted = false;   // (wave 0) no piece left to claim in this call
     bool failed = false;      // this workgroup gave up waiting (sticky, uniform)
 
     for (int64_t t = vid; t < num_tiles; t += G) {
@@ -319,21 +325,42 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(KParams p)
         // Loads of K step kb into one stage.  The resource is re-based by kb*BK elements and shrunk
         // by as many bytes, so rows past the tile's valid rows read zeros; a chunk past K reads
         // zeros through an out-of-range offset.
-        auto issue = [&](int64_t kb, char* sa, char* sb) {
+        // Loads of K step kb into one stage: 8 + 8 DMA operations of 16 bytes per lane.  The
+        // resource is re-based by kb*BK elements and shrunk by as many bytes, so rows past the
+        // tile's valid rows read zeros; a 16-byte chunk past K starts its offsets at the tile's full
+        // byte size, at or beyond this step's resource size, so it reads zeros (no branch per lane).
+        struct Dma {
+            __amdgpu_buffer_rsrc_t ra, rb;
+            uint32_t va, vb;
+            char *sa, *sb;
+            bool on;
+        };
+        auto dma_setup = [&](bool on, int64_t kb, char* sa, char* sb) {
+            Dma d;
             const uint32_t kbyte = (uint32_t)(kb * BK * 2);
-            const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base + kbyte, a_bytes - kbyte);
-            const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base + kbyte, b_bytes - kbyte);
-            // a 16-byte chunk past K starts its offsets at the tile's full byte size, which is at
-            // or beyond this step's resource size: the load returns zeros (no branch per lane)
+            d.ra = make_rsrc(a_base + kbyte, a_bytes - kbyte);
+            d.rb = make_rsrc(b_base + kbyte, b_bytes - kbyte);
             const bool kval = (int64_t)kb * BK + cchunk * 8 < K;
-            const uint32_t va = kval ? voff0 : a_bytes;
-            const uint32_t vb = kval ? voff0 : b_bytes;
+            d.va = kval ? voff0 : a_bytes;
+            d.vb = kval ? voff0 : b_bytes;
+            d.sa = sa;
+            d.sb = sb;
+            d.on = on;
+            return d;
+        };
+        auto dma_op = [&](const Dma& d, int q) {
+            if (!d.on)
+                return;
+            if (q < 8)
+                dma16(d.ra, d.sa + q * 4096 + lds_wave_off, d.va + q * row_stride32);
+            else
+                dma16(d.rb, d.sb + (q - 8) * 4096 + lds_wave_off, d.vb + (q - 8) * row_stride32);
+        };
+        auto issue_all = [&](int64_t kb, char* sa, char* sb) {
+            const Dma d = dma_setup(true, kb, sa, sb);
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                dma16(ra, sa + j * 4096 + lds_wave_off, va + j * row_stride32);
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                dma16(rb, sb + j * 4096 + lds_wave_off, vb + j * row_stride32);
+            for (int q = 0; q < 16; ++q)
+                dma_op(d, q);
         };
 
         // Fragments of two k-substeps in flight: the reads of substep kk+1 are issued before
@@ -347,29 +374,40 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(KParams p)
             for (int j = 0; j < 4; ++j)
                 bfr[j] = *reinterpret_cast<const bf16x8*>(sb + b_off[kk] + j * 4096);
         };
-        auto mfma_block = [&](const bf16x8* af, const bf16x8* bfr) {
+        // 16 MFMAs of one k-substep; with `ndma` > 0, DMA operations q0, q0+1, ... of the next
+        // stage go out between them (one per 16 / ndma MFMAs) instead of in one burst, so the
+        // texture path never backs up into this wave's instruction issue.
+        auto mfma_block = [&](const bf16x8* af, const bf16x8* bfr, const Dma& d, int q0, int ndma) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+            for (int g = 0; g < 16; ++g) {
+                const int i = g >> 2, j = g & 3;
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
+                if (ndma > 0 && (g + 1) % (16 / ndma) == 0) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    dma_op(d, q0 + (g + 1) / (16 / ndma) - 1);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            }
         };
-        auto compute = [&](const char* sa, const char* sb) {
+        // One K step out of stage (sa, sb) while the loads of the next step fill the other stage:
+        // all 16 DMA operations go out during the first two substeps, which leaves the last two
+        // (1024 MFMA cycles) for them to land before the next barrier.
+        auto compute = [&](const char* sa, const char* sb, const Dma& d) {
             bf16x8 a0[4], b0[4], a1[4], b1[4];
             load_frags(sa, sb, 0, a0, b0);
             load_frags(sa, sb, 1, a1, b1);
             __builtin_amdgcn_sched_barrier(0);
-            mfma_block(a0, b0);
+            mfma_block(a0, b0, d, 0, 8);
             __builtin_amdgcn_sched_barrier(0);
             load_frags(sa, sb, 2, a0, b0);
             __builtin_amdgcn_sched_barrier(0);
-            mfma_block(a1, b1);
+            mfma_block(a1, b1, d, 8, 8);
             __builtin_amdgcn_sched_barrier(0);
             load_frags(sa, sb, 3, a1, b1);
             __builtin_amdgcn_sched_barrier(0);
-            mfma_block(a0, b0);
+            mfma_block(a0, b0, d, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
-            mfma_block(a1, b1);
+            mfma_block(a1, b1, d, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
         };
 
@@ -377,26 +415,21 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(KParams p)
         // stage 1, so the pair loop always computes twice per iteration (one accumulator PHI).
         int64_t kb = 0;
         if (nk & 1) {
-            issue(0, sA1, sB1);
+            issue_all(0, sA1, sB1);
             wait_vmcnt0();
             __syncthreads();
-            if (nk > 1)
-                issue(1, sA0, sB0);
-            compute(sA1, sB1);
+            compute(sA1, sB1, dma_setup(nk > 1, 1, sA0, sB0));
             kb = 1;
         } else if (nk > 0) {
-            issue(0, sA0, sB0);
+            issue_all(0, sA0, sB0);
         }
         for (; kb < nk; kb += 2) {
             wait_vmcnt0();
             __syncthreads();
-            issue(kb + 1, sA1, sB1);
-            compute(sA0, sB0);
+            compute(sA0, sB0, dma_setup(true, kb + 1, sA1, sB1));
             wait_vmcnt0();
             __syncthreads();
-            if (kb + 2 < nk)
-                issue(kb + 2, sA0, sB0);
-            compute(sA1, sB1);
+            compute(sA1, sB1, dma_setup(kb + 2 < nk, kb + 2, sA0, sB0));
         }
         __syncthreads();   // all waves done with the LDS before the next tile's loads
 
@@ -470,8 +503,7 @@ __global__ __launch_bounds__(NT) void producer_kernel(KParams p)
     __shared__ int64_t s_cmd;
     const int tid = threadIdx.x;
     const bool wave0 = __builtin_amdgcn_readfirstlane(tid >> 6) == 0;
-    bool exhausted = false;
-    drain_pieces(p, tid, wave0, &s_cmd, exhausted);
+    drain_pieces(p, tid, wave0, &s_cmd);
 }
 
 __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v)
