@@ -20,7 +20,7 @@ struct Workspace {
     uint32_t* flags = nullptr;   // progress flags, one per chunk
     uint32_t* done = nullptr;    // finished pieces per chunk
     int64_t nflags = 0;
-    uint32_t* ctl = nullptr;     // [0] piece counter, [4..7] status word
+    uint32_t* ctl = nullptr;     // [0] overlapped-copy piece counter, [1] fill counter, [4..7] status
     uint32_t epoch = 0;          // value of a raised flag in the last call
     hipEvent_t last = nullptr;   // completion of the last call that used this workspace
     bool used = false;
@@ -253,13 +253,22 @@ extern "C" int ag_gemm_ex(const void* const* shards, int32_t N, int64_t M, int64
             g.copy_pieces = 0;
             AG_HIP(launch_gemm(g, kGemmFused, s), "launch fused gemm");
         } else {
-            // Producer on the side stream, GEMM on the caller's; both claim pieces from one
-            // counter, reset first.  The call ends when both have.
+            // Pipeline fill: the chunks the first wave of tiles reads are copied by the whole GPU
+            // before the GEMM starts.  The rest is copied by a producer on the side stream while
+            // the GEMM runs on the caller's; both claim those pieces from one counter, which
+            // starts where the fill stopped.  The call ends when both kernels have.
             g.copy_pieces = 1;
-            AG_HIP(launch_fill_u32(w->ctl, 1, 0u, s), "reset piece counter");
+            int cus = 0;
+            AG_HIP(device_cus(&cus), "hipDeviceGetAttribute");
+            const int64_t total = copy_pieces_total(g);
+            const int64_t fill = opt && opt->reverse_order ? 0 : first_wave_pieces(g);
+            AG_HIP(launch_set_pair(w->ctl, (uint32_t)fill, 0u, s), "reset piece counters");
+            if (fill > 0)
+                AG_HIP(launch_producer(g, w->ctl + 1, fill, cus, true, s), "launch fill copy");
             AG_HIP(hipEventRecord(w->fork, s), "hipEventRecord(fork)");
             AG_HIP(hipStreamWaitEvent(w->side, w->fork, 0), "hipStreamWaitEvent(side)");
-            AG_HIP(launch_producer(g, w->side), "launch producer");
+            if (total > fill)
+                AG_HIP(launch_producer(g, w->ctl, total, cus, false, w->side), "launch producer");
             AG_HIP(launch_gemm(g, kGemmFused, s), "launch fused gemm");
             AG_HIP(hipEventRecord(w->join, w->side), "hipEventRecord(join)");
             AG_HIP(hipStreamWaitEvent(s, w->join, 0), "hipStreamWaitEvent(join)");

@@ -46,14 +46,15 @@ struct TileCoord {
     int64_t tile;
 };
 
-__device__ __forceinline__ TileCoord tile_of(int64_t t, int num_pid_m, int num_pid_n, int pivot)
+__host__ __device__ __forceinline__ TileCoord tile_of(int64_t t, int num_pid_m, int num_pid_n, int pivot)
 {
     // grouped order, then rotation of pid_m so the walk starts at the local shard; the rotation
     // is a bijection on pid_m, so the grouping (and its L2 reuse) is kept
     const int64_t per_group = (int64_t)GROUP_M * num_pid_n;
     const int64_t group = t / per_group;
     const int64_t first_m = group * GROUP_M;
-    const int64_t rows = min((int64_t)GROUP_M, (int64_t)num_pid_m - first_m);
+    const int64_t left = (int64_t)num_pid_m - first_m;
+    const int64_t rows = left < GROUP_M ? left : (int64_t)GROUP_M;
     const int64_t in_group = t - group * per_group;
     int64_t pid_m = first_m + in_group % rows;
     const int64_t pid_n = in_group / rows;
@@ -69,6 +70,8 @@ struct KParams {
     GemmArgs a;
     int num_pid_m, num_pid_n, pivot;
     int64_t S, nchunks, piece_rows, ppc, npieces;
+    uint32_t* claim;     // piece counter this launch claims from
+    int64_t claim_end;   // pieces [counter start, claim_end) belong to this launch
 };
 
 // --------------------------------------------------------------------------------- producer
@@ -103,11 +106,11 @@ __device__ __forceinline__ Piece piece_of(const KParams& p, int64_t q)
     return pc;
 }
 
-// All threads: copy piece q with 16-byte loads/stores (8 in flight per lane), drain this wave's
+// All threads: copy piece q with 16-byte loads/stores (U in flight per lane), drain this wave's
 // stores, then a barrier -- after it, wave 0's release covers the whole piece.
+template <int U = 8>
 __device__ void copy_piece_rows(const KParams& p, int64_t q, int tid)
 {
-    constexpr int U = 8;
     const Piece pc = piece_of(p, q);
     int64_t u = tid;
     for (; u + (U - 1) * NT < pc.units; u += U * NT) {
@@ -156,8 +159,8 @@ __device__ int64_t claim_next(const KParams& p, bool& exhausted)
     if (exhausted || !p.a.copy_pieces)
         return -1;
     const uint32_t t = uniform_u32(
-        __hip_atomic_fetch_add(&p.a.ticket[0], lane0_one(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    if (t < (uint32_t)p.npieces)
+        __hip_atomic_fetch_add(p.claim, lane0_one(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    if (t < (uint32_t)p.claim_end)
         return (int64_t)t;
     exhausted = true;
     return -1;
@@ -229,6 +232,7 @@ __device__ void wait_rows(const KParams& p, int64_t m0, int64_t m1, int64_t tile
 }
 
 // Producer loop: claim, copy, publish until no piece is left.  Same loop shape as wait_rows.
+template <int U>
 __device__ void drain_pieces(const KParams& p, int tid, bool wave0, int64_t* s_cmd)
 {
     bool exhausted = false;
@@ -240,7 +244,7 @@ __device__ void drain_pieces(const KParams& p, int tid, bool wave0, int64_t* s_c
         __syncthreads();
         if (q < 0)
             break;
-        copy_piece_rows(p, q, tid);
+        copy_piece_rows<U>(p, q, tid);
         if (wave0) {
             publish_piece(p, q);
             *s_cmd = claim_next(p, exhausted);
@@ -494,16 +498,26 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(KParams p)
 
 }
 
-// Producer of the fused schedule, on its own stream: claims pieces in ready order from the same
-// counter the GEMM's waiting workgroups use, copies them and raises the chunk flags.  It never
-// waits on anything.  Small (no LDS tile, few VGPRs), so its workgroups fit beside the GEMM's on
-// every CU and the copy overlaps the MFMA work.
+// Copy kernel of the fused schedule.  Beside the GEMM (U = 8) it is small -- no LDS tile, few
+// VGPRs -- so its workgroups fit next to the GEMM's on every CU and the copy overlaps the MFMA work;
+// it claims pieces in ready order from the same counter as the GEMM's waiting workgroups and never
+// waits on anything.  Alone on the GPU, for the pipeline fill (U = 16), it keeps more loads in
+// flight per lane.
+template <int U>
 __global__ __launch_bounds__(NT) void producer_kernel(KParams p)
 {
     __shared__ int64_t s_cmd;
     const int tid = threadIdx.x;
     const bool wave0 = __builtin_amdgcn_readfirstlane(tid >> 6) == 0;
-    drain_pieces(p, tid, wave0, &s_cmd);
+    drain_pieces<U>(p, tid, wave0, &s_cmd);
+}
+
+__global__ void set_pair_kernel(uint32_t* p, uint32_t v0, uint32_t v1)
+{
+    if (threadIdx.x == 0)
+        p[0] = v0;
+    else if (threadIdx.x == 1)
+        p[1] = v1;
 }
 
 __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v)
@@ -537,7 +551,24 @@ KParams make_params(const GemmArgs& a, GemmMode mode)
         p.ppc = (a.cb + p.piece_rows - 1) / p.piece_rows;
         p.npieces = a.copy_pieces ? p.nchunks * p.ppc : 0;
     }
+    p.claim = a.ticket;
+    p.claim_end = p.npieces;
     return p;
+}
+
+int gemm_grid(const KParams& p, int cus)
+{
+    const int64_t tiles = (int64_t)p.num_pid_m * p.num_pid_n;
+    return (int)std::max<int64_t>(1, std::min<int64_t>(tiles, cus));
+}
+
+// Ready-order position of chunk c (inverse of the mapping in piece_of).
+int64_t ready_pos(const KParams& p, int64_t c)
+{
+    const int64_t r = c / p.S, s = c - r * p.S;
+    const int64_t step = ((r - p.a.local_rank - 1) % p.a.nshards + p.a.nshards) % p.a.nshards;
+    const int64_t pos = step * p.S + s;
+    return p.a.reverse_order ? p.nchunks - 1 - pos : pos;
 }
 
 hipError_t num_cus(int* out)
@@ -578,8 +609,7 @@ hipError_t launch_gemm(const GemmArgs& a, GemmMode mode, hipStream_t stream)
     if (e != hipSuccess)
         return e;
     const KParams p = make_params(a, mode);
-    const int64_t tiles = (int64_t)p.num_pid_m * p.num_pid_n;
-    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(tiles, cus));
+    const int grid = gemm_grid(p, cus);
     if (mode == kGemmFused)
         gemm_kernel<kGemmFused><<<grid, NT, 0, stream>>>(p);
     else
@@ -587,18 +617,58 @@ hipError_t launch_gemm(const GemmArgs& a, GemmMode mode, hipStream_t stream)
     return hipGetLastError();
 }
 
-hipError_t launch_producer(const GemmArgs& a, hipStream_t stream)
+int64_t copy_pieces_total(const GemmArgs& a)
+{
+    return make_params(a, kGemmFused).npieces;
+}
+
+int64_t first_wave_pieces(const GemmArgs& a)
 {
     int cus = 0;
-    hipError_t e = num_cus(&cus);
-    if (e != hipSuccess)
-        return e;
+    if (num_cus(&cus) != hipSuccess)
+        return 0;
     const KParams p = make_params(a, kGemmFused);
     if (p.npieces <= 0)
+        return 0;
+    const int64_t lo = (int64_t)a.local_rank * a.H, hi = lo + a.H;
+    const int64_t tiles = (int64_t)p.num_pid_m * p.num_pid_n;
+    const int64_t first = std::min<int64_t>(tiles, gemm_grid(p, cus));
+    int64_t last_pos = -1;
+    for (int64_t t = 0; t < first; ++t) {
+        const TileCoord tc = tile_of(t, p.num_pid_m, p.num_pid_n, p.pivot);
+        const int64_t m1 = std::min<int64_t>(tc.m0 + BM, a.M);
+        if (tc.m0 >= lo && m1 <= hi)
+            continue;
+        const int64_t c0 = (tc.m0 / a.H) * p.S + (tc.m0 % a.H) / a.cb;
+        const int64_t c1 = ((m1 - 1) / a.H) * p.S + ((m1 - 1) % a.H) / a.cb;
+        for (int64_t c = c0; c <= c1; ++c)
+            last_pos = std::max(last_pos, ready_pos(p, c));
+    }
+    return (last_pos + 1) * p.ppc;
+}
+
+hipError_t launch_producer(const GemmArgs& a, uint32_t* counter, int64_t end, int max_grid, bool alone,
+                           hipStream_t stream)
+{
+    KParams p = make_params(a, kGemmFused);
+    p.claim = counter;
+    p.claim_end = std::min(end, p.npieces);
+    if (p.claim_end <= 0)
         return hipSuccess;
-    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(p.npieces, cus));
-    producer_kernel<<<grid, NT, 0, stream>>>(p);
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(p.claim_end, max_grid));
+    if (alone)
+        producer_kernel<16><<<grid, NT, 0, stream>>>(p);
+    else
+        producer_kernel<8><<<grid, NT, 0, stream>>>(p);
     return hipGetLastError();
 }
+
+hipError_t launch_set_pair(uint32_t* p, uint32_t v0, uint32_t v1, hipStream_t stream)
+{
+    set_pair_kernel<<<1, 64, 0, stream>>>(p, v0, v1);
+    return hipGetLastError();
+}
+
+hipError_t device_cus(int* out) { return num_cus(out); }
 
 }  // namespace ag
