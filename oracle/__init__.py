@@ -29,7 +29,7 @@ def build(force: bool = True) -> str:
     """Compile oracle.c with gcc into liboracle.so next to it and return its path."""
     if force or not os.path.exists(_SO):
         tmp = _SO + ".tmp%d" % os.getpid()
-        cmd = ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-std=c11",
+        cmd = ["gcc", "-O3", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-std=c11",
                "-Wall", "-Wextra", "-shared", "-fPIC", _SRC, "-o", tmp]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _SO)
@@ -56,6 +56,10 @@ def lib() -> ctypes.CDLL:
         L.oracle_ag_gemm_at.restype = ctypes.c_int
         L.oracle_ag_gemm.argtypes = [_vp, ctypes.c_int, _i64, _i64, _vp, _i64, _vp, _vp]
         L.oracle_ag_gemm.restype = ctypes.c_int
+        L.oracle_gemm_f32_fast.argtypes = [_vp, _vp, _i64, _i64, _i64, _vp]
+        L.oracle_gemm_f32_fast.restype = None
+        L.oracle_ag_gemm_fast.argtypes = [_vp, ctypes.c_int, _i64, _i64, _vp, _i64, _vp]
+        L.oracle_ag_gemm_fast.restype = ctypes.c_int
         L.oracle_chunk_of_row.argtypes = [_i64, _i64, _i64]
         L.oracle_chunk_of_row.restype = _i64
         L.oracle_chunks_overlapping.argtypes = [_i64, _i64, _i64, _i64, _vp, _i64]
@@ -137,6 +141,33 @@ def ag_gemm(shards, B: np.ndarray):
     if rc != 0:
         raise ValueError("oracle_ag_gemm rc=%d" % rc)
     return A, C
+
+
+def gemm_f32_fast(A: np.ndarray, B: np.ndarray) -> np.ndarray:
+    """gemm_f32's C bit for bit, in a blocked loop order (for the full-size workloads)."""
+    A, B = _as_u16(A), _as_u16(B)
+    M, K = A.shape
+    Nc, K2 = B.shape
+    assert K == K2
+    C = np.empty((M, Nc), dtype=np.float32)
+    rows = (ctypes.c_void_p * max(M, 1))(*[A.ctypes.data + m * K * 2 for m in range(M)])
+    lib().oracle_gemm_f32_fast(ctypes.cast(rows, _vp), _ptr(B), M, Nc, K, _ptr(C))
+    return C
+
+
+def ag_gemm_fast(shards, B: np.ndarray) -> np.ndarray:
+    """C (M,Nc) fp32 of gather(shards) @ B^T, bit for bit ag_gemm's C, in the blocked loop order."""
+    shards = [_as_u16(s) for s in shards]
+    B = _as_u16(B)
+    H, K = shards[0].shape
+    M = H * len(shards)
+    Nc = B.shape[0]
+    C = np.empty((M, Nc), dtype=np.float32)
+    ptrs = _ptr_array(shards)
+    rc = lib().oracle_ag_gemm_fast(ctypes.cast(ptrs, _vp), len(shards), M, K, _ptr(B), Nc, _ptr(C))
+    if rc != 0:
+        raise ValueError("oracle_ag_gemm_fast rc=%d" % rc)
+    return C
 
 
 def ag_gemm_at(shards, B: np.ndarray, ms, ns) -> np.ndarray:

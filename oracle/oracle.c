@@ -4,7 +4,8 @@
  * TEST INFRASTRUCTURE ONLY: loaded by the test suite, the smoke check and the benchmark's CPU
  * baseline, never by the GPU library.  It shares no code, header or table with the HIP path.
  *
- * Build: gcc -O2 -fopenmp -ffp-contract=off -shared -fPIC oracle.c -o liboracle.so
+ * Build: gcc -O3 -fopenmp -ffp-contract=off -fno-fast-math -shared -fPIC oracle.c -o liboracle.so
+ * (no -march: the library may run on another host; the blocked GEMM picks AVX2 at run time)
  * (-ffp-contract=off keeps every multiply and add a separately rounded fp32 operation).
  *
  * Every function states the passage of the two pages it follows; see oracle.h for the page
@@ -80,6 +81,118 @@ void oracle_gemm_f32(const uint16_t *A, const uint16_t *B, int64_t M, int64_t Nc
             C[m * Nc + n] = dot_ascending_f32(A + m * K, B + n * K, K);
 }
 
+/*
+ * The same C as oracle_gemm_f32, bit for bit, computed in a cache-friendly loop order so that
+ * C for the full-size workloads (up to 10^12 multiply-adds) can be checked element by element.
+ * Only the loop nest differs: every C[m][n] still starts at 0.0f and adds the products
+ * float(A[m][k]) * float(B[n][k]) one at a time in ascending k, each product and each sum
+ * rounded to fp32 on its own (no FMA: -ffp-contract=off).  The running sum of an element is
+ * kept in a register across a block of k and in memory between blocks; storing an fp32 value and
+ * loading it back is exact, so this is the recursive summation above with its order unchanged
+ * (no partial sums, no reassociation).  The loops run over (m, n) blocks in parallel.
+ */
+enum { FAST_MB = 4, FAST_NB = 16, FAST_KC = 256, FAST_NP = 256, FAST_RB = 64 };
+
+/* acc[i][j] (i < FAST_MB, j < FAST_NB) continues its ascending-k sums over k in [k0, k0 + nk).
+ * a[i] points at row i of A (bf16 bits), bt at Bt[k0][j0] (row stride ldb floats). */
+typedef float fast_v8 __attribute__((vector_size(32)));   /* 8 independent fp32 lanes */
+
+#define FAST_MICRO_BODY                                                                  \
+    fast_v8 r[FAST_MB][2];                                                               \
+    for (int i = 0; i < FAST_MB; ++i) {                                                  \
+        memcpy(&r[i][0], &acc[i][0], sizeof(fast_v8));                                   \
+        memcpy(&r[i][1], &acc[i][8], sizeof(fast_v8));                                   \
+    }                                                                                    \
+    for (int64_t kk = 0; kk < nk; ++kk) {                                                \
+        fast_v8 b0, b1;                                                                  \
+        memcpy(&b0, bt + kk * ldb, sizeof b0);                                           \
+        memcpy(&b1, bt + kk * ldb + 8, sizeof b1);                                       \
+        for (int i = 0; i < FAST_MB; ++i) {                                              \
+            const float av = oracle_bf16_to_f32(a[i][k0 + kk]);                          \
+            const fast_v8 p0 = b0 * av, p1 = b1 * av;      /* products, one rounding */  \
+            r[i][0] = r[i][0] + p0;                        /* then the sums */           \
+            r[i][1] = r[i][1] + p1;                                                      \
+        }                                                                                \
+    }                                                                                    \
+    for (int i = 0; i < FAST_MB; ++i) {                                                  \
+        memcpy(&acc[i][0], &r[i][0], sizeof(fast_v8));                                   \
+        memcpy(&acc[i][8], &r[i][1], sizeof(fast_v8));                                   \
+    }
+
+/* acc[i][j] (i < FAST_MB, j < FAST_NB = 16) continues its ascending-k sums over k in
+ * [k0, k0 + nk).  a[i] points at row i of A (bf16 bits), bt at Bt[k0][j0] (row stride ldb
+ * floats).  Each vector lane is one element's own sum, so lanes never mix. */
+__attribute__((target("avx2"))) static void fast_micro_avx2(float acc[FAST_MB][FAST_NB],
+    const uint16_t *const a[FAST_MB], const float *bt, int64_t ldb, int64_t k0, int64_t nk)
+{
+    FAST_MICRO_BODY
+}
+
+static void fast_micro_base(float acc[FAST_MB][FAST_NB], const uint16_t *const a[FAST_MB],
+                            const float *bt, int64_t ldb, int64_t k0, int64_t nk)
+{
+    FAST_MICRO_BODY
+}
+
+void oracle_gemm_f32_fast(const uint16_t *const *a_rows, const uint16_t *B, int64_t M, int64_t Nc,
+                          int64_t K, float *C)
+{
+    /* Bt[k][n] = float(B[n][k]): the k-th row of Bt holds every column's k-th weight */
+    float *Bt = (float *)malloc(sizeof(float) * (size_t)(K > 0 ? K : 1) * (size_t)(Nc > 0 ? Nc : 1));
+    if (!Bt)
+        abort();
+#pragma omp parallel for schedule(static)
+    for (int64_t k = 0; k < K; ++k)
+        for (int64_t n = 0; n < Nc; ++n)
+            Bt[k * Nc + n] = oracle_bf16_to_f32(B[n * K + k]);
+    const int use_avx2 = __builtin_cpu_supports("avx2");
+    const int64_t n_rb = (M + FAST_RB - 1) / FAST_RB, n_np = (Nc + FAST_NP - 1) / FAST_NP;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t blk = 0; blk < n_rb * n_np; ++blk) {
+        const int64_t m0 = (blk / n_np) * FAST_RB, n0 = (blk % n_np) * FAST_NP;
+        const int64_t m1 = m0 + FAST_RB < M ? m0 + FAST_RB : M;
+        const int64_t n1 = n0 + FAST_NP < Nc ? n0 + FAST_NP : Nc;
+        for (int64_t m = m0; m < m1; ++m)
+            for (int64_t n = n0; n < n1; ++n)
+                C[m * Nc + n] = 0.0f;
+        for (int64_t k0 = 0; k0 < K; k0 += FAST_KC) {              /* ascending k blocks */
+            const int64_t k1 = k0 + FAST_KC < K ? k0 + FAST_KC : K;
+            for (int64_t mi = m0; mi < m1; mi += FAST_MB)
+                for (int64_t nj = n0; nj < n1; nj += FAST_NB) {
+                    const int64_t rows = m1 - mi < FAST_MB ? m1 - mi : FAST_MB;
+                    const int64_t cols = n1 - nj < FAST_NB ? n1 - nj : FAST_NB;
+                    float acc[FAST_MB][FAST_NB];
+                    float pad[FAST_NB];
+                    const uint16_t *a[FAST_MB];
+                    for (int i = 0; i < FAST_MB; ++i) {
+                        a[i] = a_rows[mi + (i < rows ? i : 0)];   /* short tile: repeat row 0 */
+                        for (int j = 0; j < FAST_NB; ++j)
+                            acc[i][j] = (i < rows && j < cols) ? C[(mi + i) * Nc + nj + j] : 0.0f;
+                    }
+                    if (cols < FAST_NB) {
+                        /* ragged column edge: one k at a time on a zero-padded copy of the row */
+                        for (int64_t k = k0; k < k1; ++k) {
+                            for (int j = 0; j < FAST_NB; ++j)
+                                pad[j] = j < cols ? Bt[k * Nc + nj + j] : 0.0f;
+                            if (use_avx2)
+                                fast_micro_avx2(acc, a, pad, FAST_NB, k, 1);
+                            else
+                                fast_micro_base(acc, a, pad, FAST_NB, k, 1);
+                        }
+                    } else if (use_avx2) {
+                        fast_micro_avx2(acc, a, Bt + k0 * Nc + nj, Nc, k0, k1 - k0);
+                    } else {
+                        fast_micro_base(acc, a, Bt + k0 * Nc + nj, Nc, k0, k1 - k0);
+                    }
+                    for (int i = 0; i < rows; ++i)
+                        for (int j = 0; j < cols; ++j)
+                            C[(mi + i) * Nc + nj + j] = acc[i][j];
+                }
+        }
+    }
+    free(Bt);
+}
+
 /* Row m of the gathered A: row m % H of shard m / H ([AGMM] §从集合通信理解数据流, AllGather
  * concatenates the shards in rank order; [TGATH] §二 with D0=D1=D2=1). */
 static const uint16_t *gathered_row(const uint16_t *const *shards, int64_t H, int64_t K, int64_t m)
@@ -116,6 +229,24 @@ int oracle_ag_gemm(const uint16_t *const *shards, int nshards, int64_t M, int64_
     if (rc != 0)
         return rc;
     oracle_gemm_f32(A_out, B, M, Nc, K, C);
+    return 0;
+}
+
+/* oracle_ag_gemm's C through oracle_gemm_f32_fast (the gathered A is never materialised: row m
+ * is read from its shard). */
+int oracle_ag_gemm_fast(const uint16_t *const *shards, int nshards, int64_t M, int64_t K,
+                        const uint16_t *B, int64_t Nc, float *C)
+{
+    if (nshards <= 0 || M % nshards != 0 || K < 0 || Nc < 0)
+        return -1;
+    const int64_t H = M / nshards;
+    const uint16_t **rows = (const uint16_t **)malloc(sizeof(uint16_t *) * (size_t)(M > 0 ? M : 1));
+    if (!rows)
+        return -1;
+    for (int64_t m = 0; m < M; ++m)
+        rows[m] = gathered_row(shards, H, K, m);
+    oracle_gemm_f32_fast(rows, B, M, Nc, K, C);
+    free(rows);
     return 0;
 }
 

@@ -66,6 +66,18 @@ int oracle_ag_gemm_at(const uint16_t *const *shards, int nshards, int64_t M, int
 int oracle_ag_gemm(const uint16_t *const *shards, int nshards, int64_t M, int64_t K,
                    const uint16_t *B, int64_t Nc, uint16_t *A_out, float *C);
 
+/*
+ * Bit-identical to oracle_gemm_f32 (the same ascending-k fp32 recursive sum per element, no FMA),
+ * in a blocked loop order fast enough for the full-size workloads.  Row m of A is a_rows[m]
+ * (K bf16 values); B is (Nc,K).  Pinned bitwise against oracle_gemm_f32 in the tests.
+ */
+void oracle_gemm_f32_fast(const uint16_t *const *a_rows, const uint16_t *B, int64_t M, int64_t Nc,
+                          int64_t K, float *C);
+
+/* C = gather(shards) * B^T through oracle_gemm_f32_fast.  Returns 0 or -1. */
+int oracle_ag_gemm_fast(const uint16_t *const *shards, int nshards, int64_t M, int64_t K,
+                        const uint16_t *B, int64_t Nc, float *C);
+
 /* Comm-block ("chunk") map, [AGMM] §融合后的流水线 and §数据搬运与细粒度同步:
  * shard r is split along M into S = ceil(H/cb) blocks of cb rows (the last may be shorter);
  * block s of shard r has id r*S + s.  Returns the id of the chunk holding gathered row `row`. */

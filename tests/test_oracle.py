@@ -190,6 +190,27 @@ def test_gemm_brute_force_exact_sum(M, Nc, K, seed):
             assert abs(float(C[m, n]) - exact) <= bound, (m, n)
 
 
+@pytest.mark.parametrize("M,Nc,K,seed", [(7, 5, 3, 0), (33, 17, 300, 1), (65, 259, 257, 2), (130, 40, 1000, 3),
+                                        (1, 1, 1, 4), (5, 16, 0, 5), (300, 300, 70, 6), (64, 512, 2048, 7)])
+def test_gemm_fast_is_bitwise_the_naive_order(M, Nc, K, seed):
+    """The blocked loop order used for the full-size checks computes every element with the same
+    ascending-k fp32 recursive sum as the naive triple loop, so the two agree bit for bit on shapes
+    that leave ragged row, column and k blocks."""
+    A_t, _, B_t = workloads.make_ag_gemm_shapes(1, M, K, Nc, seed=seed)
+    naive = oracle.gemm_f32(np_of(A_t), np_of(B_t))
+    fast = oracle.gemm_f32_fast(np_of(A_t), np_of(B_t))
+    assert np.array_equal(naive.view(np.uint32), fast.view(np.uint32))
+
+
+def test_ag_gemm_fast_matches_gather_then_gemm():
+    """oracle.ag_gemm_fast reads A's rows from the shards without gathering them; bitwise equal to
+    the gather-then-GEMM C on a ragged multi-shard shape, including signed zeros and exact ties."""
+    A_t, shards, B_t = workloads.make_ag_gemm_shapes(5, 37, 136, 70, seed=12)
+    _, C = oracle.ag_gemm([np_of(s) for s in shards], np_of(B_t))
+    Cf = oracle.ag_gemm_fast([np_of(s) for s in shards], np_of(B_t))
+    assert np.array_equal(C.view(np.uint32), Cf.view(np.uint32))
+
+
 def test_gemm_identity_b_returns_a():
     """Special case B = I (K = Nc): every sum has one non-zero term, so C == A exactly."""
     M, K = 24, 40
