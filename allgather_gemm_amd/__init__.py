@@ -21,13 +21,16 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "aggemm.h")
 AG_OK, AG_EINVAL, AG_ENOMEM, AG_EHIP, AG_ETIMEOUT, AG_EUNSUPPORTED = 0, -1, -2, -3, -4, -5
 MODE_FUSED, MODE_UNFUSED, MODE_GEMM_ONLY = 0, 1, 2
 _MODES = {"fused": MODE_FUSED, "unfused": MODE_UNFUSED, "gemm_only": MODE_GEMM_ONLY}
+PRODUCER_IN_KERNEL, PRODUCER_SIDE_STREAM, PRODUCER_COPY_ENGINE = 0, 1, 2
+_PRODUCERS = {"in_kernel": PRODUCER_IN_KERNEL, "side_stream": PRODUCER_SIDE_STREAM,
+              "copy_engine": PRODUCER_COPY_ENGINE}
 
 _i32, _i64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
 
 
 class AgOptions(ctypes.Structure):
     _fields_ = [("mode", _i32), ("local_rank", _i32), ("a_out", _vp), ("timeout_us", _i64),
-                ("reverse_order", _i32), ("skip_producer", _i32)]
+                ("reverse_order", _i32), ("skip_producer", _i32), ("producer", _i32)]
 
 
 class AgError(RuntimeError):
@@ -58,7 +61,7 @@ def lib() -> ctypes.CDLL:
         L.tgather.argtypes = [_vp, _i32, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i32, _vp]
         L.tgather.restype = ctypes.c_int
         L.tgather_ex.argtypes = [_vp, _i32, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
-                                 _i32, _vp]
+                                 _i32, _i32, _vp]
         L.tgather_ex.restype = ctypes.c_int
         L.ag_check.argtypes = [_vp, ctypes.POINTER(_i64)]
         L.ag_check.restype = ctypes.c_int
@@ -103,8 +106,11 @@ def _check_dev(t: torch.Tensor, name: str):
 def ag_gemm(shards, B: torch.Tensor, comm_block_rows: int, C: torch.Tensor | None = None,
             mode: str = "fused", local_rank: int = 0, a_out: torch.Tensor | None = None,
             timeout_us: int = 0, reverse_order: bool = False, skip_producer: bool = False,
-            stream=None) -> torch.Tensor:
-    """C (M, Nc) bf16 = concat(shards) @ B^T.  shards: N tensors (H, K) bf16; B: (Nc, K) bf16."""
+            producer: str = "in_kernel", stream=None) -> torch.Tensor:
+    """C (M, Nc) bf16 = concat(shards) @ B^T.  shards: N tensors (H, K) bf16; B: (Nc, K) bf16.
+
+    mode: "fused" | "unfused" | "gemm_only"; producer (fused only): "in_kernel" | "side_stream" |
+    "copy_engine".  The call is asynchronous on `stream`; check() reports a wait that gave up."""
     shards = list(shards)
     N = len(shards)
     if N == 0:
@@ -125,7 +131,7 @@ def ag_gemm(shards, B: torch.Tensor, comm_block_rows: int, C: torch.Tensor | Non
     if C.dtype != torch.bfloat16 or tuple(C.shape) != (M, Nc):
         raise ValueError("C must be (M, Nc) bfloat16")
     opt = AgOptions(_MODES[mode], local_rank, a_out.data_ptr() if a_out is not None else None,
-                    timeout_us, int(reverse_order), int(skip_producer))
+                    timeout_us, int(reverse_order), int(skip_producer), _PRODUCERS[producer])
     if a_out is not None:
         _check_dev(a_out, "a_out")
         if a_out.dtype != torch.bfloat16 or tuple(a_out.shape) != (M, K):
@@ -152,7 +158,7 @@ def _as5d(t: torch.Tensor) -> tuple:
 
 
 def tgather(shards, valid_rows: int, valid_cols: int, dst: torch.Tensor | None = None,
-            dst_rows: int | None = None, stream=None) -> torch.Tensor:
+            dst_rows: int | None = None, root: int = 0, stream=None) -> torch.Tensor:
     """dst[d0, d1, d2, r*H + i, j] = shards[r][d0, d1, d2, i, j]; returns dst."""
     shards = list(shards)
     N = len(shards)
@@ -174,14 +180,15 @@ def tgather(shards, valid_rows: int, valid_cols: int, dst: torch.Tensor | None =
         raise ValueError("dst must hold (D0, D1, D2, dst_rows, W) elements of the shards' dtype")
     esz = shards[0].element_size()
     rc = lib().tgather_ex(ctypes.cast(_ptrs(shards), _vp), N, dst.data_ptr(), D0, D1, D2, H, W,
-                          dst_rows, valid_rows, valid_cols, esz, _stream_ptr(stream))
+                          dst_rows, valid_rows, valid_cols, esz, root, _stream_ptr(stream))
     if rc != AG_OK:
         raise AgError(rc, "tgather_ex")
     return dst
 
 
 def check(stream=None) -> tuple[int, list[int]]:
-    """Waits for the stream and returns (status, [code, chunk, tile, 0]) of the device status word."""
+    """Waits for the stream and returns (status, [code, chunk, tile, epoch]) of the device status
+    word (the first wait that gave up since the last check, and its call's flag epoch)."""
     info = (_i64 * 4)()
     rc = lib().ag_check(_stream_ptr(stream), info)
     return rc, [int(x) for x in info]

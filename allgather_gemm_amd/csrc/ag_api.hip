@@ -2,6 +2,7 @@
 // per-device workspace, epochs of the progress flags, stream ordering, and launches.
 #include "../../include/aggemm.h"
 #include "ag_internal.hpp"
+#include "ag_protocol.hpp"
 
 #include <hip/hip_runtime.h>
 
@@ -20,7 +21,7 @@ struct Workspace {
     uint32_t* flags = nullptr;   // progress flags, one per chunk
     uint32_t* done = nullptr;    // finished pieces per chunk
     int64_t nflags = 0;
-    uint32_t* ctl = nullptr;     // [0] overlapped-copy piece counter, [1] fill counter, [4..7] status
+    uint32_t* ctl = nullptr;     // [0] fill piece counter, [1] piece counter of the rest, [4..7] status
     uint32_t epoch = 0;          // value of a raised flag in the last call
     hipEvent_t last = nullptr;   // completion of the last call that used this workspace
     bool used = false;
@@ -106,11 +107,13 @@ int ensure_a(Workspace& w, size_t bytes)
     return AG_OK;
 }
 
-// Next flag value; on wrap-around the flags are cleared so an old value cannot match.
+// Next flag value; on wrap-around the flags and the give-up word are cleared so an old value cannot
+// match.
 int next_epoch(Workspace& w, hipStream_t s)
 {
     if (++w.epoch == 0) {
         AG_HIP(launch_fill_u32(w.flags, w.nflags, 0u, s), "fill flags");
+        AG_HIP(launch_fill_u32(w.ctl + 7, 1, 0u, s), "clear give-up epoch");
         w.epoch = 1;
     }
     return AG_OK;
@@ -141,7 +144,8 @@ int validate_gemm(const void* const* shards, int32_t N, int64_t M, int64_t K, co
         return AG_EUNSUPPORTED;
     if (opt) {
         if (opt->mode < AG_MODE_FUSED || opt->mode > AG_MODE_GEMM_ONLY || opt->local_rank < 0 ||
-            opt->local_rank >= N || opt->skip_producer < 0 || opt->skip_producer > 1)
+            opt->local_rank >= N || opt->skip_producer < 0 || opt->skip_producer > 1 ||
+            opt->producer < AG_PRODUCER_IN_KERNEL || opt->producer > AG_PRODUCER_COPY_ENGINE)
             return AG_EINVAL;
         if (opt->mode == AG_MODE_GEMM_ONLY && !opt->a_out)
             return AG_EINVAL;
@@ -222,7 +226,7 @@ extern "C" int ag_gemm_ex(const void* const* shards, int32_t N, int64_t M, int64
 
     if (K == 0) {
         // empty reduction: C = 0, nothing to gather
-        AG_HIP(launch_gemm(g, kGemmPlain, s), "launch gemm");
+        AG_HIP(launch_gemm(g, kGemmPlain, nullptr, s), "launch gemm");
         return end_use(*w, s);
     }
     if (mode == AG_MODE_UNFUSED) {
@@ -240,39 +244,60 @@ extern "C" int ag_gemm_ex(const void* const* shards, int32_t N, int64_t M, int64
         d.valid_rows = H;
         d.valid_cols = K;
         AG_HIP(launch_tgather(d, s), "launch tgather");
-        AG_HIP(launch_gemm(g, kGemmPlain, s), "launch gemm");
-    } else {
-        if ((rc = next_epoch(*w, s)) != AG_OK)
-            return rc;
-        g.epoch = w->epoch;
-        if (mode == AG_MODE_GEMM_ONLY) {
+        AG_HIP(launch_gemm(g, kGemmPlain, nullptr, s), "launch gemm");
+        return end_use(*w, s);
+    }
+    if ((rc = next_epoch(*w, s)) != AG_OK)
+        return rc;
+    g.epoch = w->epoch;
+    const int producer = opt ? opt->producer : AG_PRODUCER_IN_KERNEL;
+    if (mode == AG_MODE_GEMM_ONLY || (opt && opt->skip_producer)) {
+        // every flag raised beforehand (GEMM-only), or none ever (test of the give-up path)
+        if (mode == AG_MODE_GEMM_ONLY)
             AG_HIP(launch_fill_u32(w->flags, nchunks, g.epoch, s), "fill flags");
-            g.copy_pieces = 0;
-            AG_HIP(launch_gemm(g, kGemmFused, s), "launch fused gemm");
-        } else if (opt && opt->skip_producer) {
-            g.copy_pieces = 0;
-            AG_HIP(launch_gemm(g, kGemmFused, s), "launch fused gemm");
-        } else {
-            // Pipeline fill: the chunks the first wave of tiles reads are copied by the whole GPU
-            // before the GEMM starts.  The rest is copied by a producer on the side stream while
-            // the GEMM runs on the caller's; both claim those pieces from one counter, which
-            // starts where the fill stopped.  The call ends when both kernels have.
-            g.copy_pieces = 1;
-            int cus = 0;
-            AG_HIP(device_cus(&cus), "hipDeviceGetAttribute");
-            const int64_t total = copy_pieces_total(g);
-            const int64_t fill = opt && opt->reverse_order ? 0 : first_wave_pieces(g);
-            AG_HIP(launch_set_pair(w->ctl, (uint32_t)fill, 0u, s), "reset piece counters");
-            if (fill > 0)
-                AG_HIP(launch_producer(g, w->ctl + 1, fill, cus, true, s), "launch fill copy");
-            AG_HIP(hipEventRecord(w->fork, s), "hipEventRecord(fork)");
-            AG_HIP(hipStreamWaitEvent(w->side, w->fork, 0), "hipStreamWaitEvent(side)");
-            if (total > fill)
-                AG_HIP(launch_producer(g, w->ctl, total, cus, false, w->side), "launch producer");
-            AG_HIP(launch_gemm(g, kGemmFused, s), "launch fused gemm");
-            AG_HIP(hipEventRecord(w->join, w->side), "hipEventRecord(join)");
-            AG_HIP(hipStreamWaitEvent(s, w->join, 0), "hipStreamWaitEvent(join)");
+        g.copy_pieces = kCopyNone;
+        AG_HIP(launch_gemm(g, kGemmFused, nullptr, s), "launch fused gemm");
+    } else if (producer == AG_PRODUCER_IN_KERNEL) {
+        g.copy_pieces = kCopyInKernel;
+        const FusedPlan f = plan_fused(g);
+        AG_HIP(launch_reset(g, f, s), "reset piece counters");
+        AG_HIP(launch_gemm(g, kGemmFused, &f, s), "launch fused gemm");
+    } else if (producer == AG_PRODUCER_SIDE_STREAM) {
+        // the first wave's chunks are copied by the whole GPU before the GEMM starts; the rest by a
+        // copy kernel on the side stream while the GEMM runs (waiting tiles help); the call ends
+        // when both kernels have
+        g.copy_pieces = kCopyWaiters;
+        const FusedPlan f = plan_fused(g);
+        AG_HIP(launch_reset(g, f, s), "reset piece counters");
+        if (f.fill_end > 0)
+            AG_HIP(launch_producer(g, f, true, s), "launch fill copy");
+        AG_HIP(hipEventRecord(w->fork, s), "hipEventRecord(fork)");
+        AG_HIP(hipStreamWaitEvent(w->side, w->fork, 0), "hipStreamWaitEvent(side)");
+        AG_HIP(launch_producer(g, f, false, w->side), "launch producer");
+        AG_HIP(launch_gemm(g, kGemmFused, &f, s), "launch fused gemm");
+        AG_HIP(hipEventRecord(w->join, w->side), "hipEventRecord(join)");
+        AG_HIP(hipStreamWaitEvent(s, w->join, 0), "hipStreamWaitEvent(join)");
+    } else {
+        // copy engines: per chunk in ready order, a copy that uses no compute units, then the
+        // chunk's flag written by the stream once the copy has completed
+        g.copy_pieces = kCopyNone;
+        AG_HIP(hipEventRecord(w->fork, s), "hipEventRecord(fork)");
+        AG_HIP(hipStreamWaitEvent(w->side, w->fork, 0), "hipStreamWaitEvent(side)");
+        AG_HIP(launch_gemm(g, kGemmFused, nullptr, s), "launch fused gemm");
+        const PieceMap pm = pm_make(H, comm_block_rows, N, g.local_rank, K, gemm_tile_m(), 1);
+        for (int64_t pos = 0; pos < pm.nchunks; ++pos) {
+            const int64_t c = pm_ready_chunk(pm, pos);
+            int64_t first = 0, last = 0;
+            pm_chunk_rows(pm, c, first, last);
+            const int64_t r = c / pm.S;
+            const char* src = static_cast<const char*>(shards[r]) + (first - r * H) * K * 2;
+            char* dst = static_cast<char*>(a_buf) + first * K * 2;
+            AG_HIP(hipMemcpyAsync(dst, src, (size_t)((last - first) * K * 2), hipMemcpyDeviceToDeviceNoCU,
+                                  w->side), "hipMemcpyAsync(copy engine)");
+            AG_HIP(hipStreamWriteValue32(w->side, w->flags + c, g.epoch, 0), "hipStreamWriteValue32(flag)");
         }
+        AG_HIP(hipEventRecord(w->join, w->side), "hipEventRecord(join)");
+        AG_HIP(hipStreamWaitEvent(s, w->join, 0), "hipStreamWaitEvent(join)");
     }
     return end_use(*w, s);
 }
@@ -295,9 +320,11 @@ extern "C" int ag_gemm_unfused(const void* const* shards, int32_t N, int64_t M, 
 
 extern "C" int tgather_ex(const void* const* shards, int32_t N, void* dst, int64_t D0, int64_t D1,
                           int64_t D2, int64_t H, int64_t W, int64_t dst_rows, int64_t valid_rows,
-                          int64_t valid_cols, int32_t elem_size, void* stream)
+                          int64_t valid_cols, int32_t elem_size, int32_t root, void* stream)
 {
     if (!shards || N < 1 || N > kMaxShards || D0 < 0 || D1 < 0 || D2 < 0 || H < 0 || W < 0)
+        return AG_EINVAL;
+    if (root < 0 || root >= N)
         return AG_EINVAL;
     if (valid_rows < 1 || valid_cols < 1)
         return AG_EINVAL;
@@ -334,7 +361,7 @@ extern "C" int tgather(const void* const* shards, int32_t N, void* dst, int64_t 
                        int32_t elem_size, void* stream)
 {
     return tgather_ex(shards, N, dst, D0, D1, D2, H, W, (int64_t)N * H, valid_rows, valid_cols,
-                      elem_size, stream);
+                      elem_size, 0, stream);
 }
 
 extern "C" int ag_check(void* stream, int64_t info[4])
@@ -352,11 +379,8 @@ extern "C" int ag_check(void* stream, int64_t info[4])
             info[i] = st[i];
     if (st[0] == 0)
         return AG_OK;
-    AG_HIP(hipMemset(w->ctl + 4, 0, 4 * sizeof(uint32_t)), "hipMemset(status)");
-    // a wait that gave up leaves piece counters of that call in an unknown state
-    AG_HIP(hipMemset(w->ctl, 0, 2 * sizeof(uint32_t)), "hipMemset(ticket)");
-    if (w->done)
-        AG_HIP(hipMemset(w->done, 0, w->nflags * sizeof(uint32_t)), "hipMemset(done)");
+    // the reported failure is consumed; counters need no repair (every call resets its own)
+    AG_HIP(hipMemset(w->ctl + 4, 0, 3 * sizeof(uint32_t)), "hipMemset(status)");
     return AG_ETIMEOUT;
 }
 

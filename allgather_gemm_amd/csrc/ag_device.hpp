@@ -88,10 +88,13 @@ __device__ __forceinline__ void flag_publish(uint32_t* f, uint32_t value)
 
 __device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 
-// Status word: the first failure wins (0 = clean).  Layout: [code, chunk, tile, 0].  Called by
-// all 64 lanes of one wave: lane 0 contributes the code, the others OR in zero, and the
-// follow-up writes repeat one value, so there is no one-lane branch.
-__device__ __forceinline__ void report_failure(uint32_t* status, uint32_t code, uint32_t chunk, uint32_t tile)
+// Status word [code, chunk, tile, epoch]: the first failure since the host last read it wins the
+// first three words (what ag_check reports); the fourth always takes the failing call's epoch, so
+// the other waits of that call -- and only of that call -- give up at once.  Called by all 64
+// lanes of one wave: lane 0 contributes the code, the others OR in zero, and the follow-up writes
+// repeat one value, so there is no one-lane branch.
+__device__ __forceinline__ void report_failure(uint32_t* status, uint32_t code, uint32_t chunk, uint32_t tile,
+                                               uint32_t epoch)
 {
     const uint32_t mine = (threadIdx.x & 63) == 0 ? code : 0u;
     const uint32_t prev = __builtin_amdgcn_readfirstlane(
@@ -100,6 +103,7 @@ __device__ __forceinline__ void report_failure(uint32_t* status, uint32_t code, 
         (void)__hip_atomic_exchange(&status[1], chunk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         (void)__hip_atomic_exchange(&status[2], tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    (void)__hip_atomic_exchange(&status[3], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace ag

@@ -1,5 +1,5 @@
 // ag_gemm.hip -- persistent bf16 MFMA GEMM (fp32 accumulate) for C = A * B^T on gfx950, with
-// the chunked-AllGather consumer/producer logic of the fused schedule.
+// the chunked-AllGather consumer and copy logic of the fused schedule.
 //
 // What it computes follows the fused AllGather+MatMul article ("Triton第四课：基于对称内存融合
 // AllGather 与 MatMul，提速1.56倍"):
@@ -8,20 +8,30 @@
 //    the shard, every other tile first waits for the flags of the chunks its rows overlap and then
 //    reads the aggregate A buffer;
 //  * section 数据搬运与细粒度同步: a chunk's flag is raised only after its rows have landed;
-//  * section wait_signal 的实现与语义: one lane polls, then a workgroup barrier releases the block.
-// The producer runs on a second stream (section 融合后的流水线 has the copy on a backend stream
-// beside the MatMul): a small copy kernel whose workgroups sit next to the GEMM's on every CU.
-// The chunk copies are split into pieces claimed from one counter, in ready order, by the
-// producer's workgroups and also by any GEMM workgroup that would otherwise wait.  A piece is
-// claimed only by a running workgroup, so no wait can deadlock whatever the two grids' residency
-// or launch order: a GEMM that starts alone copies what it needs itself.
+//  * section wait_signal 的实现与语义: one wave polls, then a workgroup barrier releases the block.
+// The article's copy runs beside the MatMul on its own engine.  Here the copy is done by the GEMM's
+// own workgroups, in pieces (contiguous byte ranges, see ag_protocol.hpp) handed out in ready order
+// from counters in device memory:
+//  * a workgroup whose tile finds a chunk unpublished copies pieces at full speed until the chunk is
+//    ready (the pipeline fill at the start is done this way, from a counter only waiters use);
+//  * every running wave also copies one piece of its own in the background, 1 KiB per K step: the
+//    store of the previous step's slice and the load of the next slice go out right after the step's
+//    barrier, next to the tile loads, and the piece is published once its stores have drained.
+// A wave finishes its piece before its workgroup can wait on anything, and waiters only take pieces
+// they copy at once, so every handed-out piece is published in bounded time: no wait can deadlock.
+// Before a workgroup exits it copies whatever no one has taken yet (the gathered output needs
+// every chunk, also those no tile waits for).
+// Other producers (a copy kernel on a second stream, the copy engines) leave the counters alone and
+// only raise the flags; the GEMM then just waits.
 //
 // Tiling (gfx950): 256x256 output tile per 256-thread workgroup (4 waves, 2x2, 128x128 each),
 // K step 64, v_mfma_f32_32x32x16_bf16, A/B tiles staged in LDS by buffer_load ... lds (16 B per
 // lane, no VGPR round trip), double-buffered (2 x 64 KiB).  LDS rows are 128 B (64 bf16) and
-// their 16-byte chunks are XOR-swizzled so the ds_read_b128 fragment loads are conflict-free.
+// their 16-byte chunks are XOR-swizzled so the ds_read_b128 fragment loads are conflict-free
+// (every bank serves at most four dwords of a wave's read).
 #include "ag_device.hpp"
 #include "ag_internal.hpp"
+#include "ag_protocol.hpp"
 
 #include <algorithm>
 
@@ -33,9 +43,12 @@ constexpr int NT = 256;                        // threads per workgroup
 constexpr int SLOTS = BM * BK * 2 / 16;        // 16-byte slots per operand tile (2048)
 constexpr int TILE_BYTES = SLOTS * 16;         // 32 KiB per operand tile
 constexpr int GROUP_M = 8;                     // tile rows per group of the grouped order
-constexpr int64_t PIECE_BYTES = 64 * 1024;     // target bytes per copy piece
+constexpr int64_t PIECE_BYTES = 16 * 1024;     // bytes per copy piece
+constexpr int WAIT_BATCH = 4;                  // pieces a waiting workgroup takes at a time
+constexpr int SLICE = 1024;                    // bytes a wave copies per K step in the background
 
 static_assert(BM == BN, "A and B tiles share one LDS layout");
+static_assert(PIECE_BYTES % SLICE == 0, "a piece is a whole number of slices");
 
 // Swizzle of the 16-byte chunk index inside a 128-byte LDS row: depends on row bits 0..3 so that
 // any 8 (and any 16) consecutive rows reading the same logical chunk hit distinct banks.
@@ -48,17 +61,8 @@ struct TileCoord {
 
 __host__ __device__ __forceinline__ TileCoord tile_of(int64_t t, int num_pid_m, int num_pid_n, int pivot)
 {
-    // grouped order, then rotation of pid_m so the walk starts at the local shard; the rotation
-    // is a bijection on pid_m, so the grouping (and its L2 reuse) is kept
-    const int64_t per_group = (int64_t)GROUP_M * num_pid_n;
-    const int64_t group = t / per_group;
-    const int64_t first_m = group * GROUP_M;
-    const int64_t left = (int64_t)num_pid_m - first_m;
-    const int64_t rows = left < GROUP_M ? left : (int64_t)GROUP_M;
-    const int64_t in_group = t - group * per_group;
-    int64_t pid_m = first_m + in_group % rows;
-    const int64_t pid_n = in_group / rows;
-    pid_m = (pid_m + pivot) % num_pid_m;
+    int64_t pid_m, pid_n;
+    pm_tile_of(t, num_pid_m, num_pid_n, pivot, GROUP_M, pid_m, pid_n);
     TileCoord c;
     c.m0 = pid_m * BM;
     c.n0 = pid_n * BN;
@@ -69,119 +73,122 @@ __host__ __device__ __forceinline__ TileCoord tile_of(int64_t t, int num_pid_m, 
 struct KParams {
     GemmArgs a;
     int num_pid_m, num_pid_n, pivot;
-    int64_t S, nchunks, piece_rows, ppc, npieces;
-    uint32_t* claim;     // piece counter this launch claims from
-    int64_t claim_end;   // pieces [counter start, claim_end) belong to this launch
+    PieceMap pm;
+    int64_t npieces;     // pieces of this call (0: nothing is copied by this launch's claims)
+    int64_t fill_end;    // pieces [0, fill_end) come from ctl[0], only waiting workgroups take them
+    int trickle;         // running waves copy pieces in the background
 };
 
-// --------------------------------------------------------------------------------- producer
-// Piece q of the copy: position q / ppc in ready order (shards local+1, local+2, ..., local),
-// sub-range q % ppc of that chunk's rows.  A piece is whole rows, so it is one contiguous byte
-// range in both the shard and the aggregate buffer.
-struct Piece {
-    const i32x4* src;
-    i32x4* dst;
-    int64_t units;   // 16-byte units
-    int64_t chunk;
-};
-
-__device__ __forceinline__ Piece piece_of(const KParams& p, int64_t q)
-{
-    const GemmArgs& a = p.a;
-    int64_t pos = q / p.ppc;
-    const int64_t sub = q - pos * p.ppc;
-    if (a.reverse_order)
-        pos = p.nchunks - 1 - pos;
-    const int64_t shard_step = pos / p.S, s = pos - shard_step * p.S;
-    const int r = (int)((a.local_rank + 1 + shard_step) % a.nshards);
-    const int64_t chunk_end = min((s + 1) * a.cb, a.H);
-    const int64_t row0 = min(s * a.cb + sub * p.piece_rows, chunk_end);
-    const int64_t row1 = min(row0 + p.piece_rows, chunk_end);
-    Piece pc;
-    pc.src = reinterpret_cast<const i32x4*>(static_cast<const char*>(a.shards[r]) + row0 * a.K * 2);
-    pc.dst = reinterpret_cast<i32x4*>(static_cast<char*>(const_cast<void*>(a.A)) +
-                                      ((int64_t)r * a.H + row0) * a.K * 2);
-    pc.units = (row1 - row0) * a.K * 2 / 16;
-    pc.chunk = (int64_t)r * p.S + s;
-    return pc;
-}
-
-// All threads: copy piece q with 16-byte loads/stores (U in flight per lane), drain this wave's
-// stores, then a barrier -- after it, wave 0's release covers the whole piece.
-template <int U = 8>
-__device__ void copy_piece_rows(const KParams& p, int64_t q, int tid)
-{
-    const Piece pc = piece_of(p, q);
-    int64_t u = tid;
-    for (; u + (U - 1) * NT < pc.units; u += U * NT) {
-        i32x4 v[U];
-#pragma unroll
-        for (int i = 0; i < U; ++i)
-            v[i] = pc.src[u + i * NT];
-#pragma unroll
-        for (int i = 0; i < U; ++i)
-            pc.dst[u + i * NT] = v[i];
-    }
-    for (; u < pc.units; u += NT)
-        pc.dst[u] = pc.src[u];
-    wait_vmcnt0();
-    __syncthreads();
-}
-
-// The single-writer steps below run on all 64 lanes of wave 0 (a wave-uniform branch), never on
+// --------------------------------------------------------------------------------- copy pieces
+// The single-writer steps below run on all 64 lanes of a wave (a wave-uniform branch), never on
 // one lane: a one-lane branch inside a loop that also holds barriers lets the compiler's control
 // flow structurizer peel that lane out of the loop while the other lanes keep iterating.  Counters
-// take +1 from lane 0 and +0 from the others, every result is read from lane 0, and the
+// take +n from lane 0 and +0 from the others, every result is read from lane 0, and the
 // remaining writes (exchange, compare-exchange, LDS store) repeat the same value.
-__device__ __forceinline__ uint32_t lane0_one() { return (threadIdx.x & 63) == 0 ? 1u : 0u; }
+__device__ __forceinline__ uint32_t lane0_n(uint32_t n) { return (threadIdx.x & 63) == 0 ? n : 0u; }
 
 __device__ __forceinline__ uint32_t uniform_u32(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
-// Wave 0: count piece q as done; the last piece of its chunk raises the chunk's flag.
-__device__ void publish_piece(const KParams& p, int64_t q)
+// Ready-order piece index -> piece (the stress mode hands pieces out back to front).
+__device__ __forceinline__ PieceSpan piece_at(const KParams& p, int64_t q)
+{
+    return pm_piece(p.pm, p.a.reverse_order ? p.npieces - 1 - q : q);
+}
+
+// One wave: n more pieces of chunk c are complete (their stores drained); the last of the chunk's
+// pieces raises its flag.  Release on the counter orders this wave's stores (and, through the
+// workgroup barrier that precedes a workgroup copy, the other waves') before the count.
+__device__ void publish(const KParams& p, int64_t c, uint32_t n)
 {
     const GemmArgs& a = p.a;
-    const int64_t c = piece_of(p, q).chunk;
     const uint32_t old = uniform_u32(
-        __hip_atomic_fetch_add(&a.done[c], lane0_one(), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT));
-    if (old + 1 == (uint32_t)p.ppc) {
+        __hip_atomic_fetch_add(&a.done[c], lane0_n(n), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT));
+    if (old + n == (uint32_t)p.pm.ppc) {
         // the other pieces' releases are in this counter's release sequence: acquire them (once
-        // per chunk, not per piece) so the flag's release below covers their rows too
+        // per chunk) so the flag's release below covers their bytes too
         acquire_agent();
-        (void)__hip_atomic_exchange(&a.done[c], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         flag_publish(&a.flags[c], a.epoch);
     }
 }
 
-// Wave 0: next piece to copy, or -1 when none is left (then `exhausted` sticks).
-__device__ int64_t claim_next(const KParams& p, bool& exhausted)
+// Publishes pieces [q0, q0 + n), grouping consecutive pieces of one chunk into one count.
+__device__ void publish_range(const KParams& p, int64_t q0, int64_t n)
 {
-    if (exhausted || !p.a.copy_pieces)
-        return -1;
+    int64_t q = q0;
+    while (q < q0 + n) {
+        const int64_t c = piece_at(p, q).chunk;
+        int64_t e = q + 1;
+        while (e < q0 + n && piece_at(p, e).chunk == c)
+            ++e;
+        publish(p, c, (uint32_t)(e - q));
+        q = e;
+    }
+}
+
+// One wave: takes up to `want` pieces from a counter that hands out [start, end); returns the first
+// piece and sets *n (0 when the counter is spent).
+__device__ __forceinline__ int64_t take(uint32_t* ctr, int64_t end, uint32_t want, int64_t* n)
+{
     const uint32_t t = uniform_u32(
-        __hip_atomic_fetch_add(p.claim, lane0_one(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    if (t < (uint32_t)p.claim_end)
-        return (int64_t)t;
-    exhausted = true;
-    return -1;
+        __hip_atomic_fetch_add(ctr, lane0_n(want), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    const int64_t avail = end - (int64_t)t;
+    *n = avail <= 0 ? 0 : (avail < (int64_t)want ? avail : (int64_t)want);
+    return (int64_t)t;
+}
+
+// All threads of the workgroup: copy pieces [q0, q0 + n) with 16-byte loads/stores (U in flight per
+// lane), drain, barrier.  After it, one wave's release covers every byte.
+template <int U = 8>
+__device__ void copy_pieces(const KParams& p, int64_t q0, int64_t n, int tid)
+{
+    for (int64_t q = q0; q < q0 + n; ++q) {
+        const PieceSpan sp = piece_at(p, q);
+        const i32x4* src = reinterpret_cast<const i32x4*>(static_cast<const char*>(p.a.shards[sp.shard]) + sp.src_off);
+        i32x4* dst = reinterpret_cast<i32x4*>(static_cast<char*>(const_cast<void*>(p.a.A)) + sp.dst_off);
+        const int64_t units = sp.bytes / 16;
+        int64_t u = tid;
+        for (; u + (U - 1) * NT < units; u += U * NT) {
+            i32x4 v[U];
+#pragma unroll
+            for (int i = 0; i < U; ++i)
+                v[i] = src[u + i * NT];
+#pragma unroll
+            for (int i = 0; i < U; ++i)
+                dst[u + i * NT] = v[i];
+        }
+        for (; u < units; u += NT)
+            dst[u] = src[u];
+    }
+    wait_vmcnt0();
+    __syncthreads();
 }
 
 constexpr int64_t kReady = -1, kIdle = -2, kFailed = -3;
 
-// Wave 0: what the workgroup does next while it waits for chunk c: kReady, kFailed, a piece to
-// copy, or kIdle (sleep and ask again).  Gives up after spin_limit ticks of the 100 MHz clock.
-__device__ int64_t decide_wait(const KParams& p, int64_t c, uint64_t t_start, int64_t tile, bool& exhausted)
+// Wave 0 of a waiting workgroup: what to do next while chunk c is not ready -- kReady, kFailed, a
+// batch of pieces to copy (returned as its first piece, count in *n), or kIdle (sleep, ask again).
+// Gives up after spin_limit ticks of the 100 MHz clock; a failure is tagged with this call's epoch
+// so only this call's other waits give up early.
+__device__ int64_t decide_wait(const KParams& p, int64_t c, uint64_t t_start, int64_t tile, bool& exhausted,
+                               int64_t* n)
 {
     const GemmArgs& a = p.a;
+    *n = 0;
     if (uniform_u32(flag_peek(&a.flags[c])) == a.epoch)
         return kReady;
-    if (uniform_u32(flag_peek(&a.status[0])) != 0)
-        return kFailed;                                  // another workgroup gave up
-    const int64_t q = claim_next(p, exhausted);
-    if (q >= 0)
-        return q;
+    if (uniform_u32(flag_peek(&a.status[3])) == a.epoch)
+        return kFailed;                                  // another workgroup of this call gave up
+    if (!exhausted && p.npieces > 0) {
+        int64_t q = take(a.ticket, p.fill_end, WAIT_BATCH, n);
+        if (*n > 0)
+            return q;
+        q = take(a.ticket + 1, p.npieces, WAIT_BATCH, n);
+        if (*n > 0)
+            return q;
+        exhausted = true;
+    }
     if ((int64_t)(__builtin_amdgcn_s_memrealtime() - t_start) > a.spin_limit) {
-        report_failure(a.status, 1u, (uint32_t)c, (uint32_t)tile);
+        report_failure(a.status, 1u, (uint32_t)c, (uint32_t)tile, a.epoch);
         return kFailed;
     }
     return kIdle;
@@ -197,18 +204,21 @@ __device__ int64_t decide_wait(const KParams& p, int64_t c, uint64_t t_start, in
 __device__ void wait_rows(const KParams& p, int64_t m0, int64_t m1, int64_t tile, int tid, bool wave0,
                           int64_t* s_cmd, bool& exhausted, bool& failed)
 {
-    const GemmArgs& a = p.a;
-    const int64_t c_first = (m0 / a.H) * p.S + (m0 % a.H) / a.cb;
-    const int64_t c_last = ((m1 - 1) / a.H) * p.S + ((m1 - 1) % a.H) / a.cb;
+    int64_t c_first, c_last;
+    pm_chunks_of_rows(p.pm, m0, m1, c_first, c_last);
     for (int64_t c = c_first; c <= c_last; ++c) {
         if (failed)
             break;
         const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
-        if (wave0)
-            *s_cmd = decide_wait(p, c, t_start, tile, exhausted);
+        if (wave0) {
+            int64_t n;
+            s_cmd[0] = decide_wait(p, c, t_start, tile, exhausted, &n);
+            s_cmd[1] = n;
+        }
         for (;;) {
             barrier_after_lds_write();
-            const int64_t cmd = uniform_i64(*s_cmd);
+            const int64_t cmd = uniform_i64(s_cmd[0]);
+            const int64_t cnt = uniform_i64(s_cmd[1]);
             __syncthreads();
             if (cmd == kReady)
                 break;
@@ -217,13 +227,15 @@ __device__ void wait_rows(const KParams& p, int64_t m0, int64_t m1, int64_t tile
                 break;
             }
             if (cmd >= 0)
-                copy_piece_rows(p, cmd, tid);
+                copy_pieces(p, cmd, cnt, tid);
             else
                 __builtin_amdgcn_s_sleep(4);
             if (wave0) {
                 if (cmd >= 0)
-                    publish_piece(p, cmd);
-                *s_cmd = decide_wait(p, c, t_start, tile, exhausted);
+                    publish_range(p, cmd, cnt);
+                int64_t n;
+                s_cmd[0] = decide_wait(p, c, t_start, tile, exhausted, &n);
+                s_cmd[1] = n;
             }
         }
     }
@@ -231,23 +243,133 @@ __device__ void wait_rows(const KParams& p, int64_t m0, int64_t m1, int64_t tile
     __syncthreads();
 }
 
-// Producer loop: claim, copy, publish until no piece is left.  Same loop shape as wait_rows.
-template <int U>
-__device__ void drain_pieces(const KParams& p, int tid, bool wave0, int64_t* s_cmd)
+// ------------------------------------------------------------------------- background copy
+// Per-wave state (wave-uniform): the piece being copied, how far its loads got, the slice loaded
+// in the last step and not yet stored, and a piece whose last store went out in the last step.
+struct Trickle {
+    int64_t q;            // piece being copied, -1 none
+    int64_t bytes;        // its size
+    int64_t off;          // next byte to load
+    int64_t pend;         // byte offset of the slice held in `data`, -1 none
+    int64_t publish_q;    // piece to publish at the next step (its stores drained meanwhile)
+    const char* src;
+    char* dst;
+    i32x4 data;
+    bool exhausted;
+};
+
+__device__ __forceinline__ void trickle_take(const KParams& p, Trickle& tr)
 {
-    bool exhausted = false;
-    if (wave0)
-        *s_cmd = claim_next(p, exhausted);
+    int64_t n;
+    const int64_t q = take(p.a.ticket + 1, p.npieces, 1, &n);
+    if (n == 0) {
+        tr.exhausted = true;
+        return;
+    }
+    const PieceSpan sp = piece_at(p, q);
+    tr.q = q;
+    tr.bytes = sp.bytes;
+    tr.off = 0;
+    tr.src = static_cast<const char*>(p.a.shards[sp.shard]) + sp.src_off;
+    tr.dst = static_cast<char*>(const_cast<void*>(p.a.A)) + sp.dst_off;
+}
+
+// One K step of the background copy; called by every lane of the wave right after the step's
+// barrier, when this wave's loads and stores of the previous step have drained.
+__device__ void trickle_step(const KParams& p, Trickle& tr, int lane)
+{
+    if (tr.publish_q >= 0) {
+        publish(p, piece_at(p, tr.publish_q).chunk, 1);
+        tr.publish_q = -1;
+    }
+    if (tr.pend >= 0) {
+        const int64_t b = tr.pend + 16 * lane;
+        if (b < tr.bytes)
+            *reinterpret_cast<i32x4*>(tr.dst + b) = tr.data;
+        if (tr.pend + SLICE >= tr.bytes) {       // that was the piece's last slice
+            tr.publish_q = tr.q;
+            tr.q = -1;
+        }
+        tr.pend = -1;
+    }
+    if (tr.q < 0 && !tr.exhausted)
+        trickle_take(p, tr);
+    if (tr.q >= 0) {
+        if (tr.bytes == 0) {                     // empty piece past a short chunk's end
+            tr.publish_q = tr.q;
+            tr.q = -1;
+        } else {
+            const int64_t b = tr.off + 16 * lane;
+            if (b < tr.bytes)
+                tr.data = *reinterpret_cast<const i32x4*>(tr.src + b);
+            tr.pend = tr.off;
+            tr.off += SLICE;
+        }
+    }
+}
+
+// Finishes this wave's piece at full speed and publishes everything it holds (per wave, no
+// barrier): called before the workgroup waits on a chunk and when the kernel ends.
+__device__ void trickle_flush(const KParams& p, Trickle& tr, int lane)
+{
+    if (tr.pend >= 0) {
+        const int64_t b = tr.pend + 16 * lane;
+        if (b < tr.bytes)
+            *reinterpret_cast<i32x4*>(tr.dst + b) = tr.data;
+        tr.pend = -1;
+    }
+    if (tr.q >= 0) {
+        // the rest of the piece, four slices in flight per lane
+        for (int64_t o = tr.off; o < tr.bytes; o += 4 * SLICE) {
+            i32x4 v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t b = o + i * SLICE + 16 * lane;
+                if (b < tr.bytes)
+                    v[i] = *reinterpret_cast<const i32x4*>(tr.src + b);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int64_t b = o + i * SLICE + 16 * lane;
+                if (b < tr.bytes)
+                    *reinterpret_cast<i32x4*>(tr.dst + b) = v[i];
+            }
+        }
+    }
+    wait_vmcnt0();
+    if (tr.publish_q >= 0) {
+        publish(p, piece_at(p, tr.publish_q).chunk, 1);
+        tr.publish_q = -1;
+    }
+    if (tr.q >= 0) {
+        publish(p, piece_at(p, tr.q).chunk, 1);
+        tr.q = -1;
+    }
+}
+
+// Copy kernel run beside the GEMM (or before it), taking pieces from one counter: the same loop
+// shape as wait_rows, never waiting on anything.
+template <int U>
+__device__ void drain_pieces(const KParams& p, uint32_t* ctr, int64_t end, int tid, bool wave0, int64_t* s_cmd)
+{
+    if (wave0) {
+        int64_t n;
+        s_cmd[0] = take(ctr, end, WAIT_BATCH, &n);
+        s_cmd[1] = n;
+    }
     for (;;) {
         barrier_after_lds_write();
-        const int64_t q = uniform_i64(*s_cmd);
+        const int64_t q = uniform_i64(s_cmd[0]);
+        const int64_t n = uniform_i64(s_cmd[1]);
         __syncthreads();
-        if (q < 0)
+        if (n <= 0)
             break;
-        copy_piece_rows<U>(p, q, tid);
+        copy_pieces<U>(p, q, n, tid);
         if (wave0) {
-            publish_piece(p, q);
-            *s_cmd = claim_next(p, exhausted);
+            publish_range(p, q, n);
+            int64_t m;
+            s_cmd[0] = take(ctr, end, WAIT_BATCH, &m);
+            s_cmd[1] = m;
         }
     }
 }
@@ -260,7 +382,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(KParams p)
     __shared__ __attribute__((aligned(1024))) char sB0[TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) char sA1[TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) char sB1[TILE_BYTES];
-    __shared__ int64_t s_cmd;
+    __shared__ int64_t s_cmd[2];
 
     const GemmArgs& a = p.a;
     const int tid = threadIdx.x;
@@ -297,6 +419,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(KParams p)
 
     bool exhausted = false;   // (wave 0) no piece left to claim in this call
     bool failed = false;      // this workgroup gave up waiting (sticky, uniform)
+    Trickle tr;               // this wave's in-loop copy (wave-uniform state)
+    tr.q = -1;
+    tr.pend = -1;
+    tr.publish_q = -1;
+    tr.exhausted = !(MODE == kGemmFused && p.trickle);
 
     for (int64_t t = vid; t < num_tiles; t += G) {
         const TileCoord tc = tile_of(t, p.num_pid_m, p.num_pid_n, p.pivot);
@@ -307,8 +434,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(KParams p)
             a_base = static_cast<const char*>(a.shards[a.local_rank]) + (tc.m0 - lo) * K * 2;
             a_rows = m1 - tc.m0;
         } else {
-            if (MODE == kGemmFused)
-                wait_rows(p, tc.m0, m1, t, tid, wave0, &s_cmd, exhausted, failed);
+            if (MODE == kGemmFused) {
+                trickle_flush(p, tr, lane);          // a piece this wave holds never waits on anything
+                wait_rows(p, tc.m0, m1, t, tid, wave0, s_cmd, exhausted, failed);
+            }
             a_base = static_cast<const char*>(a.A) + tc.m0 * K * 2;
             a_rows = m1 - tc.m0;
         }
@@ -417,11 +546,16 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(KParams p)
 
         // Double-buffered K loop.  With an odd number of K steps the first one runs alone out of
         // stage 1, so the pair loop always computes twice per iteration (one accumulator PHI).
+        // Every K step starts after the drain of this wave's loads and stores and a barrier; the
+        // in-loop copy (fused schedule) issues its store and its next load right there, so both
+        // have a whole step to land.
         int64_t kb = 0;
         if (nk & 1) {
             issue_all(0, sA1, sB1);
             wait_vmcnt0();
             __syncthreads();
+            if (MODE == kGemmFused)
+                trickle_step(p, tr, lane);
             compute(sA1, sB1, dma_setup(nk > 1, 1, sA0, sB0));
             kb = 1;
         } else if (nk > 0) {
@@ -430,9 +564,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(KParams p)
         for (; kb < nk; kb += 2) {
             wait_vmcnt0();
             __syncthreads();
+            if (MODE == kGemmFused)
+                trickle_step(p, tr, lane);
             compute(sA0, sB0, dma_setup(true, kb + 1, sA1, sB1));
             wait_vmcnt0();
             __syncthreads();
+            if (MODE == kGemmFused)
+                trickle_step(p, tr, lane);
             compute(sA1, sB1, dma_setup(kb + 2 < nk, kb + 2, sA0, sB0));
         }
         __syncthreads();   // all waves done with the LDS before the next tile's loads
@@ -495,29 +633,41 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(KParams p)
         }
         __syncthreads();   // LDS is free again for the next tile's loads
     }
-
+    if (MODE == kGemmFused) {
+        // the gathered output needs every chunk, also those no tile waited for: before it exits,
+        // the workgroup copies whatever is still unclaimed
+        trickle_flush(p, tr, lane);
+        if (p.npieces > 0) {
+            drain_pieces<8>(p, a.ticket, p.fill_end, tid, wave0, s_cmd);
+            drain_pieces<8>(p, a.ticket + 1, p.npieces, tid, wave0, s_cmd);
+        }
+    }
 }
 
-// Copy kernel of the fused schedule.  Beside the GEMM (U = 8) it is small -- no LDS tile, few
-// VGPRs -- so its workgroups fit next to the GEMM's on every CU and the copy overlaps the MFMA work;
-// it claims pieces in ready order from the same counter as the GEMM's waiting workgroups and never
-// waits on anything.  Alone on the GPU, for the pipeline fill (U = 16), it keeps more loads in
-// flight per lane.
+
+// Copy kernel of the side-stream schedule.  Beside the GEMM (U = 8) it is small -- no LDS tile, few
+// VGPRs -- so its workgroups fit next to the GEMM's; alone on the GPU, for the pipeline fill
+// (U = 16), it keeps more loads in flight per lane.
 template <int U>
-__global__ __launch_bounds__(NT) void producer_kernel(KParams p)
+__global__ __launch_bounds__(NT) void producer_kernel(KParams p, uint32_t* ctr, int64_t end)
 {
-    __shared__ int64_t s_cmd;
+    __shared__ int64_t s_cmd[2];
     const int tid = threadIdx.x;
     const bool wave0 = __builtin_amdgcn_readfirstlane(tid >> 6) == 0;
-    drain_pieces<U>(p, tid, wave0, &s_cmd);
+    drain_pieces<U>(p, ctr, end, tid, wave0, s_cmd);
 }
 
-__global__ void set_pair_kernel(uint32_t* p, uint32_t v0, uint32_t v1)
+// Start of a fused call: piece counters, per-chunk piece counts.  A call that gave up leaves its
+// counters in any state; every call starts from here, so the next one is unaffected.
+__global__ void reset_kernel(uint32_t* ticket, uint32_t fill_start, uint32_t main_start, uint32_t* done, int64_t n)
 {
-    if (threadIdx.x == 0)
-        p[0] = v0;
-    else if (threadIdx.x == 1)
-        p[1] = v1;
+    const int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (i == 0) {
+        ticket[0] = fill_start;
+        ticket[1] = main_start;
+    }
+    for (int64_t j = i; j < n; j += (int64_t)gridDim.x * blockDim.x)
+        done[j] = 0;
 }
 
 __global__ void fill_u32_kernel(uint32_t* p, int64_t n, uint32_t v)
@@ -536,23 +686,16 @@ KParams make_params(const GemmArgs& a, GemmMode mode)
     p.num_pid_m = (int)((a.M + BM - 1) / BM);
     p.num_pid_n = (int)((a.Nc + BN - 1) / BN);
     p.pivot = 0;
-    p.S = 1;
-    p.nchunks = 0;
-    p.piece_rows = 1;
-    p.ppc = 1;
     p.npieces = 0;
+    p.fill_end = 0;
+    p.trickle = 0;
+    p.pm = pm_make(1, 1, 1, 0, a.K, BM, PIECE_BYTES);
     if (mode == kGemmFused) {
         p.pivot = (int)(((int64_t)a.local_rank * a.H) / BM % p.num_pid_m);
-        p.S = (a.H + a.cb - 1) / a.cb;
-        p.nchunks = (int64_t)a.nshards * p.S;
-        const int64_t row_bytes = a.K * 2;
-        p.piece_rows = row_bytes > 0 ? std::max<int64_t>(1, PIECE_BYTES / row_bytes) : a.cb;
-        p.piece_rows = std::min(p.piece_rows, a.cb);
-        p.ppc = (a.cb + p.piece_rows - 1) / p.piece_rows;
-        p.npieces = a.copy_pieces ? p.nchunks * p.ppc : 0;
+        p.pm = pm_make(a.H, a.cb, a.nshards, a.local_rank, a.K, BM, PIECE_BYTES);
+        p.npieces = a.copy_pieces ? p.pm.nchunks * p.pm.ppc : 0;
+        p.trickle = a.copy_pieces == 1 ? 1 : 0;
     }
-    p.claim = a.ticket;
-    p.claim_end = p.npieces;
     return p;
 }
 
@@ -560,15 +703,6 @@ int gemm_grid(const KParams& p, int cus)
 {
     const int64_t tiles = (int64_t)p.num_pid_m * p.num_pid_n;
     return (int)std::max<int64_t>(1, std::min<int64_t>(tiles, cus));
-}
-
-// Ready-order position of chunk c (inverse of the mapping in piece_of).
-int64_t ready_pos(const KParams& p, int64_t c)
-{
-    const int64_t r = c / p.S, s = c - r * p.S;
-    const int64_t step = ((r - p.a.local_rank - 1) % p.a.nshards + p.a.nshards) % p.a.nshards;
-    const int64_t pos = step * p.S + s;
-    return p.a.reverse_order ? p.nchunks - 1 - pos : pos;
 }
 
 hipError_t num_cus(int* out)
@@ -588,6 +722,30 @@ hipError_t num_cus(int* out)
     return hipSuccess;
 }
 
+// Pieces [0, n) of the ready order hold every chunk that the first wave of GEMM tiles (one tile per
+// workgroup of the persistent grid) reads from the aggregate buffer.
+int64_t first_wave_end(const KParams& p, int cus)
+{
+    const GemmArgs& a = p.a;
+    if (p.npieces <= 0 || a.reverse_order)
+        return 0;
+    const int64_t lo = (int64_t)a.local_rank * a.H, hi = lo + a.H;
+    const int64_t tiles = (int64_t)p.num_pid_m * p.num_pid_n;
+    const int64_t first = std::min<int64_t>(tiles, gemm_grid(p, cus));
+    int64_t last_pos = -1;
+    for (int64_t t = 0; t < first; ++t) {
+        const TileCoord tc = tile_of(t, p.num_pid_m, p.num_pid_n, p.pivot);
+        const int64_t m1 = std::min<int64_t>(tc.m0 + BM, a.M);
+        if (tc.m0 >= lo && m1 <= hi)
+            continue;
+        int64_t c0, c1;
+        pm_chunks_of_rows(p.pm, tc.m0, m1, c0, c1);
+        for (int64_t c = c0; c <= c1; ++c)
+            last_pos = std::max(last_pos, pm_ready_pos(p.pm, c));
+    }
+    return (last_pos + 1) * p.pm.ppc;
+}
+
 }  // namespace
 
 int gemm_tile_m() { return BM; }
@@ -602,13 +760,38 @@ hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t s
     return hipGetLastError();
 }
 
-hipError_t launch_gemm(const GemmArgs& a, GemmMode mode, hipStream_t stream)
+FusedPlan plan_fused(const GemmArgs& a)
+{
+    FusedPlan f;
+    f.npieces = 0;
+    f.fill_end = 0;
+    f.nchunks = 0;
+    int cus = 0;
+    if (num_cus(&cus) != hipSuccess)
+        return f;
+    const KParams p = make_params(a, kGemmFused);
+    f.npieces = p.npieces;
+    f.fill_end = first_wave_end(p, cus);
+    f.nchunks = p.pm.nchunks;
+    return f;
+}
+
+hipError_t launch_reset(const GemmArgs& a, const FusedPlan& f, hipStream_t stream)
+{
+    const int blocks = (int)std::max<int64_t>(1, std::min<int64_t>((f.nchunks + 255) / 256, 256));
+    reset_kernel<<<blocks, 256, 0, stream>>>(a.ticket, 0u, (uint32_t)f.fill_end, a.done, f.nchunks);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmArgs& a, GemmMode mode, const FusedPlan* f, hipStream_t stream)
 {
     int cus = 0;
     hipError_t e = num_cus(&cus);
     if (e != hipSuccess)
         return e;
-    const KParams p = make_params(a, mode);
+    KParams p = make_params(a, mode);
+    if (f)
+        p.fill_end = f->fill_end;
     const int grid = gemm_grid(p, cus);
     if (mode == kGemmFused)
         gemm_kernel<kGemmFused><<<grid, NT, 0, stream>>>(p);
@@ -617,55 +800,24 @@ hipError_t launch_gemm(const GemmArgs& a, GemmMode mode, hipStream_t stream)
     return hipGetLastError();
 }
 
-int64_t copy_pieces_total(const GemmArgs& a)
-{
-    return make_params(a, kGemmFused).npieces;
-}
-
-int64_t first_wave_pieces(const GemmArgs& a)
+hipError_t launch_producer(const GemmArgs& a, const FusedPlan& f, bool fill, hipStream_t stream)
 {
     int cus = 0;
-    if (num_cus(&cus) != hipSuccess)
-        return 0;
-    const KParams p = make_params(a, kGemmFused);
-    if (p.npieces <= 0)
-        return 0;
-    const int64_t lo = (int64_t)a.local_rank * a.H, hi = lo + a.H;
-    const int64_t tiles = (int64_t)p.num_pid_m * p.num_pid_n;
-    const int64_t first = std::min<int64_t>(tiles, gemm_grid(p, cus));
-    int64_t last_pos = -1;
-    for (int64_t t = 0; t < first; ++t) {
-        const TileCoord tc = tile_of(t, p.num_pid_m, p.num_pid_n, p.pivot);
-        const int64_t m1 = std::min<int64_t>(tc.m0 + BM, a.M);
-        if (tc.m0 >= lo && m1 <= hi)
-            continue;
-        const int64_t c0 = (tc.m0 / a.H) * p.S + (tc.m0 % a.H) / a.cb;
-        const int64_t c1 = ((m1 - 1) / a.H) * p.S + ((m1 - 1) % a.H) / a.cb;
-        for (int64_t c = c0; c <= c1; ++c)
-            last_pos = std::max(last_pos, ready_pos(p, c));
-    }
-    return (last_pos + 1) * p.ppc;
-}
-
-hipError_t launch_producer(const GemmArgs& a, uint32_t* counter, int64_t end, int max_grid, bool alone,
-                           hipStream_t stream)
-{
+    hipError_t e = num_cus(&cus);
+    if (e != hipSuccess)
+        return e;
     KParams p = make_params(a, kGemmFused);
-    p.claim = counter;
-    p.claim_end = std::min(end, p.npieces);
-    if (p.claim_end <= 0)
+    p.fill_end = f.fill_end;
+    uint32_t* ctr = fill ? a.ticket : a.ticket + 1;
+    const int64_t first = fill ? 0 : f.fill_end, end = fill ? f.fill_end : p.npieces;
+    if (end <= first)
         return hipSuccess;
-    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(p.claim_end, max_grid));
-    if (alone)
-        producer_kernel<16><<<grid, NT, 0, stream>>>(p);
+    const int64_t batches = (end - first + WAIT_BATCH - 1) / WAIT_BATCH;
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(batches, cus));
+    if (fill)
+        producer_kernel<16><<<grid, NT, 0, stream>>>(p, ctr, end);
     else
-        producer_kernel<8><<<grid, NT, 0, stream>>>(p);
-    return hipGetLastError();
-}
-
-hipError_t launch_set_pair(uint32_t* p, uint32_t v0, uint32_t v1, hipStream_t stream)
-{
-    set_pair_kernel<<<1, 64, 0, stream>>>(p, v0, v1);
+        producer_kernel<8><<<grid, NT, 0, stream>>>(p, ctr, end);
     return hipGetLastError();
 }
 

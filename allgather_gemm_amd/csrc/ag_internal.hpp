@@ -26,6 +26,13 @@ hipError_t launch_tgather(const GatherDesc& d, hipStream_t stream);
 // ------------------------------------------------------------------------------------ GEMM
 enum GemmMode { kGemmPlain = 0, kGemmFused = 1 };
 
+// Who copies the chunks in the fused schedule (GemmArgs::copy_pieces).
+enum CopyBy {
+    kCopyNone = 0,       // someone else raises the flags (copy engines, or GEMM-only with raised flags)
+    kCopyInKernel = 1,   // waiting workgroups and a background copy in every running wave
+    kCopyWaiters = 2,    // waiting workgroups only (a copy kernel on a second stream does the rest)
+};
+
 struct GemmArgs {
     const void* A;          // gathered A (M, K): library workspace or caller buffer
     const void* B;          // (Nc, K)
@@ -38,37 +45,36 @@ struct GemmArgs {
     int64_t H;              // rows per shard
     int64_t cb;             // comm block rows
     uint32_t* flags;        // progress[nshards * S]
-    uint32_t* done;         // per-chunk finished-piece counters
-    uint32_t* ticket;       // [0] piece counter of the overlapped copy (producer and GEMM), [1] prologue's
-    uint32_t* status;       // [code, chunk, tile, spins]
+    uint32_t* done;         // per-chunk finished-piece counters (zeroed at the start of every call)
+    uint32_t* ticket;       // [0] next fill piece, [1] next piece of the rest
+    uint32_t* status;       // [code, chunk, tile, epoch of the failing call]
     uint32_t epoch;         // value a published flag holds during this call
-    int copy_pieces;        // 1: the grid also performs the copy; 0: flags are already set
-    int reverse_order;      // stress: claim pieces in reverse ready order
-    int64_t spin_limit;     // polls of one flag before giving up
+    int copy_pieces;        // CopyBy
+    int reverse_order;      // stress: hand pieces out back to front
+    int64_t spin_limit;     // 100 MHz ticks of one flag wait before giving up
 };
 
-hipError_t launch_gemm(const GemmArgs& a, GemmMode mode, hipStream_t stream);
+// Piece plan of one fused call.
+struct FusedPlan {
+    int64_t npieces;        // pieces the GEMM's counters hand out (0 if it copies nothing)
+    int64_t fill_end;       // pieces [0, fill_end): every chunk the first wave of tiles reads
+    int64_t nchunks;
+};
 
-// Copy pieces of the fused schedule: piece q is position q / ppc in ready order, sub-range q % ppc
-// of that chunk's rows.
-int64_t copy_pieces_total(const GemmArgs& a);
+FusedPlan plan_fused(const GemmArgs& a);
 
-// Pieces [0, n) hold every chunk that the first wave of GEMM tiles (one tile per workgroup of the
-// persistent grid) reads from the aggregate buffer; 0 when that wave only reads the local shard.
-int64_t first_wave_pieces(const GemmArgs& a);
+// Zeroes the per-chunk piece counts and sets the piece counters to 0 and fill_end.
+hipError_t launch_reset(const GemmArgs& a, const FusedPlan& f, hipStream_t stream);
 
-// Copy kernel of the fused schedule: its workgroups claim pieces from `counter` until it reaches
-// `end`, copy them and raise the chunk flags; at most `max_grid` workgroups.  It never waits.
-// `alone`: nothing else runs meanwhile (deeper loads); otherwise it is sized to sit beside the GEMM.
-hipError_t launch_producer(const GemmArgs& a, uint32_t* counter, int64_t end, int max_grid, bool alone,
-                           hipStream_t stream);
+hipError_t launch_gemm(const GemmArgs& a, GemmMode mode, const FusedPlan* f, hipStream_t stream);
 
-// p[0] = v0, p[1] = v1 (one tiny kernel, safe to capture in a graph).
-hipError_t launch_set_pair(uint32_t* p, uint32_t v0, uint32_t v1, hipStream_t stream);
+// Copy kernel of the side-stream schedule: with fill, pieces [0, fill_end) (alone on the GPU,
+// before the GEMM); else the rest, beside the GEMM.  It never waits.
+hipError_t launch_producer(const GemmArgs& a, const FusedPlan& f, bool fill, hipStream_t stream);
 
 hipError_t device_cus(int* out);
 
-// Small helper kernel: flags[0..n) = value (used for the GEMM-only schedule and epoch wrap).
+// Small helper kernel: p[0..n) = value (flag epochs, GEMM-only flags).
 hipError_t launch_fill_u32(uint32_t* p, int64_t n, uint32_t value, hipStream_t stream);
 
 int gemm_tile_m();

@@ -41,9 +41,19 @@ extern "C" {
 #define AG_EUNSUPPORTED -5   /* shape outside the library's limits (see each entry point) */
 
 /* Schedules of ag_gemm_ex. */
-#define AG_MODE_FUSED      0  /* chunked copy and GEMM in one persistent grid, per-chunk flags */
+#define AG_MODE_FUSED      0  /* chunked copy and GEMM overlapped, per-chunk flags */
 #define AG_MODE_UNFUSED    1  /* full gather (tgather kernel), then the GEMM: the serial schedule */
 #define AG_MODE_GEMM_ONLY  2  /* the fused GEMM with every flag already raised and no copy */
+
+/* Who copies the chunks in AG_MODE_FUSED ([AGMM] 融合后的流水线 has the copy beside the MatMul). */
+#define AG_PRODUCER_IN_KERNEL    0  /* the GEMM's workgroups: tiles that would wait copy at once, and
+                                       every running wave copies a little per K step (default) */
+#define AG_PRODUCER_SIDE_STREAM  1  /* a copy kernel on a second stream (its first-wave part runs
+                                       before the GEMM), waiting tiles help */
+#define AG_PRODUCER_COPY_ENGINE  2  /* per chunk, a device-to-device copy that uses no compute units
+                                       (hipMemcpyDeviceToDeviceNoCU) then a stream write of the flag
+                                       ([AGMM] 数据搬运与细粒度同步: copy, then stream_write_value32);
+                                       the GEMM only waits */
 
 typedef struct ag_options {
     int32_t mode;          /* AG_MODE_* */
@@ -54,7 +64,10 @@ typedef struct ag_options {
     int32_t reverse_order; /* test aid: the copy claims chunks in reverse ready order */
     int32_t skip_producer; /* test aid (AG_MODE_FUSED): copy nothing and leave the flags stale, so
                               every non-local tile's wait ends through timeout_us; ag_check then
-                              reports AG_ETIMEOUT.  C is meaningless after such a call. */
+                              reports AG_ETIMEOUT.  C is meaningless after such a call; later calls
+                              are unaffected (every call starts from fresh counters, and a give-up
+                              only short-cuts the waits of the call that gave up). */
+    int32_t producer;      /* AG_PRODUCER_* (AG_MODE_FUSED only) */
 } ag_options;
 
 /*
@@ -80,7 +93,8 @@ int ag_gemm(const void *const *shards, int32_t N, int64_t M, int64_t K, const vo
 int ag_gemm_unfused(const void *const *shards, int32_t N, int64_t M, int64_t K, const void *B,
                     int64_t Nc, void *C, int64_t comm_block_rows, void *stream);
 
-/* ag_gemm with options (NULL = defaults: fused, local_rank 0, internal buffer, 10 s). */
+/* ag_gemm with options (NULL = defaults: fused, in-kernel producer, local_rank 0, internal buffer,
+ * 10 s). */
 int ag_gemm_ex(const void *const *shards, int32_t N, int64_t M, int64_t K, const void *B,
                int64_t Nc, void *C, int64_t comm_block_rows, void *stream,
                const ag_options *opt);
@@ -102,13 +116,16 @@ int tgather(const void *const *shards, int32_t N, void *dst, int64_t D0, int64_t
             void *stream);
 
 /* tgather into a taller dst of shape (D0, D1, D2, dst_rows, W), dst_rows >= N*H; rows at or
- * beyond N*H of every plane are left untouched ([TGATH] 7.2 内存约束). */
+ * beyond N*H of every plane are left untouched ([TGATH] 7.2 内存约束).  root, 0..N-1, is the rank
+ * whose buffer dst is ([TGATH] RunGatherWithRoot): on one GPU every shard is already addressable
+ * from it, so it selects nothing and is only validated. */
 int tgather_ex(const void *const *shards, int32_t N, void *dst, int64_t D0, int64_t D1,
                int64_t D2, int64_t H, int64_t W, int64_t dst_rows, int64_t valid_rows,
-               int64_t valid_cols, int32_t elem_size, void *stream);
+               int64_t valid_cols, int32_t elem_size, int32_t root, void *stream);
 
 /* Waits for `stream`, then reads and clears the current device's status word.  Returns AG_OK,
- * or AG_ETIMEOUT with info = {code, chunk, tile, 0} for the first flag wait that gave up. */
+ * or AG_ETIMEOUT with info = {code, chunk, tile, epoch} for the first flag wait that gave up since
+ * the last ag_check (epoch: the failing call's flag value). */
 int ag_check(void *stream, int64_t info[4]);
 
 /* Static text for a return code. */

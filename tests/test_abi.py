@@ -60,11 +60,13 @@ def test_ag_gemm_rejects_unaligned_or_null():
 def test_ag_gemm_ex_rejects_bad_options():
     L = ag.lib()
     ptrs = ctypes.cast(_fake_ptrs(2), _vp)
-    for opt in (ag.AgOptions(7, 0, None, 0, 0, 0),          # unknown mode
-                ag.AgOptions(0, 2, None, 0, 0, 0),          # local rank out of range
-                ag.AgOptions(2, 0, None, 0, 0, 0),          # GEMM-only needs the gathered A
-                ag.AgOptions(0, 0, 0x40004, 0, 0, 0),       # unaligned a_out
-                ag.AgOptions(0, 0, None, 0, 0, 3)):         # skip_producer is 0 or 1
+    for opt in (ag.AgOptions(7, 0, None, 0, 0, 0, 0),       # unknown mode
+                ag.AgOptions(0, 2, None, 0, 0, 0, 0),       # local rank out of range
+                ag.AgOptions(2, 0, None, 0, 0, 0, 0),       # GEMM-only needs the gathered A
+                ag.AgOptions(0, 0, 0x40004, 0, 0, 0, 0),    # unaligned a_out
+                ag.AgOptions(0, 0, None, 0, 0, 3, 0),       # skip_producer is 0 or 1
+                ag.AgOptions(0, 0, None, 0, 0, 0, 3),       # unknown producer
+                ag.AgOptions(0, 0, None, 0, 0, 0, -1)):
         assert L.ag_gemm_ex(ptrs, 2, 8, 8, _vp(0x20000), 8, _vp(0x30000), 4, None,
                             ctypes.byref(opt)) == ag.AG_EINVAL
 
@@ -97,5 +99,14 @@ def test_tgather_ex_rejects_short_dst():
     """TGATHER deep dive §7.2: the destination must hold N*H rows."""
     L = ag.lib()
     rc = L.tgather_ex(ctypes.cast(_fake_ptrs(4), _vp), 4, _vp(0x30000), 1, 1, 1, 8, 8, 31, 8, 8, 4,
-                      None)
+                      0, None)
+    assert rc == ag.AG_EINVAL
+
+
+@pytest.mark.parametrize("root", [-1, 4, 100])
+def test_tgather_ex_rejects_root_outside_the_ranks(root):
+    """TGATHER deep dive (RunGatherWithRoot): the root is one of the N ranks."""
+    L = ag.lib()
+    rc = L.tgather_ex(ctypes.cast(_fake_ptrs(4), _vp), 4, _vp(0x30000), 1, 1, 1, 8, 8, 32, 8, 8, 4,
+                      root, None)
     assert rc == ag.AG_EINVAL

@@ -1,10 +1,10 @@
 """AG-GEMM on the GPU against the CPU oracle.
 
-C must be within |gpu - C32| <= 1e-2 + 1.6e-2 * |C32| of the oracle's fp32-accumulated result
-(element by element at small sizes; at the full workload sizes on sampled elements, the tile,
-chunk and shard boundaries included).  The gathered A must equal the oracle's gather bit for bit.
-The fused, unfused and GEMM-only schedules share the tile code and k order, so their C must agree
-bit for bit with each other.
+C must be within |gpu - C32| <= 1e-2 + 1.6e-2 * |C32| of the oracle's fp32-accumulated result,
+element by element at every size (the full workloads through the oracle's blocked loop order,
+which is bitwise its naive one).  The gathered A must equal the oracle's gather bit for bit.  The
+fused (every producer), unfused and GEMM-only schedules share the tile code and k order, so their
+C must agree bit for bit with each other.
 """
 import numpy as np
 import pytest
@@ -44,6 +44,27 @@ def run(shards_d, B_d, cb, **kw):
     return C
 
 
+PRODUCERS = ("in_kernel", "side_stream", "copy_engine")
+
+
+def assert_close_on_device(C_gpu: torch.Tensor, C32: np.ndarray, where=""):
+    """Element-wise check of a large C: the oracle's values go to the device and every element is
+    compared there (in row blocks, to bound memory)."""
+    M = C32.shape[0]
+    step = max(1, (1 << 26) // max(1, C32.shape[1]))
+    bad_total = 0
+    worst = 0.0
+    for m0 in range(0, M, step):
+        ref = torch.from_numpy(C32[m0:m0 + step]).to(C_gpu.device).double()
+        got = C_gpu[m0:m0 + step].double()
+        assert not torch.isnan(got).any(), "NaN in C " + where
+        err = (got - ref).abs()
+        bound = ATOL + RTOL * ref.abs()
+        bad_total += int((err > bound).sum())
+        worst = max(worst, float((err - bound).max()))
+    assert bad_total == 0, "%d elements out of tolerance %s (worst excess %g)" % (bad_total, where, worst)
+
+
 # ------------------------------------------------------------------------------ small, full check
 @pytest.mark.parametrize("local_rank", [0, 1, 2, 3])
 def test_tiny_workload_all_schedules(local_rank):
@@ -60,6 +81,11 @@ def test_tiny_workload_all_schedules(local_rank):
     C_g = run(sd, Bd, cfg.cb, mode="gemm_only", local_rank=local_rank, a_out=a_out)
     assert torch.equal(C_f.view(torch.int16), C_u.view(torch.int16))
     assert torch.equal(C_f.view(torch.int16), C_g.view(torch.int16))
+    for producer in PRODUCERS[1:]:
+        a2 = torch.full((cfg.M, cfg.K), float("nan"), dtype=torch.bfloat16, device=DEV)
+        C_p = run(sd, Bd, cfg.cb, local_rank=local_rank, a_out=a2, producer=producer)
+        assert np.array_equal(u16(a2), A_ref), producer
+        assert torch.equal(C_f.view(torch.int16), C_p.view(torch.int16)), producer
     rc, info = ag.check()
     assert rc == ag.AG_OK, info
 
@@ -79,12 +105,14 @@ def test_edge_shapes_full_check(N, H, K, Nc, cb, local):
     A, shards, B = workloads.make_ag_gemm_shapes(N, H, K, Nc, seed=N * 1000 + H)
     A_ref, C32 = oracle.ag_gemm([u16(s) for s in shards], u16(B))
     sd, Bd = to_dev(A, shards, B)
-    a_out = torch.full((N * H, K), float("nan"), dtype=torch.bfloat16, device=DEV)
-    C_f = run(sd, Bd, cb, local_rank=local, a_out=a_out)
-    assert np.array_equal(u16(a_out), A_ref)
-    assert_close_to_oracle(C_f, C32)
     C_u = run(sd, Bd, cb, mode="unfused")
-    assert torch.equal(C_f.view(torch.int16), C_u.view(torch.int16))
+    assert_close_to_oracle(C_u, C32, "unfused")
+    for producer in PRODUCERS:
+        a_out = torch.full((N * H, K), float("nan"), dtype=torch.bfloat16, device=DEV)
+        C_f = run(sd, Bd, cb, local_rank=local, a_out=a_out, producer=producer)
+        assert np.array_equal(u16(a_out), A_ref), producer
+        assert torch.equal(C_f.view(torch.int16), C_u.view(torch.int16)), producer
+    assert ag.check()[0] == ag.AG_OK
 
 
 def test_zero_k_gives_zero():
@@ -130,6 +158,75 @@ def test_wait_times_out_instead_of_hanging():
     assert ag.check()[0] == ag.AG_OK
 
 
+@pytest.mark.parametrize("producer", PRODUCERS)
+def test_call_after_a_timed_out_call_needs_no_check(producer):
+    """A call that gave up (no copy at all, short timeout: every kernel still exits by itself) is
+    followed by normal calls without ag_check in between: they must not inherit its failure or its
+    half-counted chunks, and ag_check must still report the earlier give-up."""
+    N, H, K, Nc, cb = 4, 256, 128, 256, 64
+    print("timeout then %s" % producer, flush=True)
+    A, shards, B = workloads.make_ag_gemm_shapes(N, H, K, Nc, seed=6)
+    A_ref, C32 = oracle.ag_gemm([u16(s) for s in shards], u16(B))
+    sd, Bd = to_dev(A, shards, B)
+    ag.ag_gemm(sd, Bd, cb, skip_producer=True, timeout_us=2000, local_rank=1)
+    for rep in range(2):
+        a_out = torch.full((N * H, K), float("nan"), dtype=torch.bfloat16, device=DEV)
+        C = run(sd, Bd, cb, a_out=a_out, producer=producer, local_rank=rep)
+        assert np.array_equal(u16(a_out), A_ref), rep
+        assert_close_to_oracle(C, C32, "call %d after the time-out" % rep)
+    rc, info = ag.check()
+    assert rc == ag.AG_ETIMEOUT and info[0] == 1
+    assert ag.check()[0] == ag.AG_OK
+
+
+@pytest.mark.parametrize("producer", PRODUCERS)
+def test_new_shard_contents_every_call(producer):
+    """Alternating inputs through one gathered buffer: every call must see its own shards' rows,
+    never rows an earlier call left in the buffer or in a cache."""
+    N, H, K, Nc, cb = 8, 160, 256, 512, 32
+    print("alternating inputs %s" % producer, flush=True)
+    sets = []
+    for seed in (41, 42):
+        A, shards, B = workloads.make_ag_gemm_shapes(N, H, K, Nc, seed=seed)
+        A_ref, C32 = oracle.ag_gemm([u16(s) for s in shards], u16(B))
+        sd, Bd = to_dev(A, shards, B)
+        sets.append((sd, Bd, A_ref, C32))
+    a_out = torch.empty((N * H, K), dtype=torch.bfloat16, device=DEV)
+    for i in range(5):
+        sd, Bd, A_ref, C32 = sets[i % 2]
+        for buf in (a_out, None):
+            C = run(sd, Bd, cb, a_out=buf, producer=producer, local_rank=i % N)
+            if buf is not None:
+                assert np.array_equal(u16(buf), A_ref), i
+            assert_close_to_oracle(C, C32, "call %d" % i)
+    assert ag.check()[0] == ag.AG_OK
+
+
+def test_more_tiles_than_compute_units_every_producer():
+    """400 output tiles (more than one per CU, so later waves of the persistent grid run), comm
+    blocks that straddle tiles and shards, element-wise against the oracle for every producer and
+    two local shards."""
+    N, H, K, Nc, cb = 8, 640, 512, 5120, 160
+    A, shards, B = workloads.make_ag_gemm_shapes(N, H, K, Nc, seed=7, b_std=0.05)
+    A_ref = np.zeros((N * H, K), dtype=np.uint16)
+    oracle.tgather([u16(s) for s in shards], A_ref, 1, 1, 1, H, K)
+    C32 = oracle.ag_gemm_fast([u16(s) for s in shards], u16(B))
+    sd, Bd = to_dev(A, shards, B)
+    ref = None
+    for producer in PRODUCERS:
+        for local in (0, 5):
+            print("400 tiles %s local=%d" % (producer, local), flush=True)
+            a_out = torch.full((N * H, K), float("nan"), dtype=torch.bfloat16, device=DEV)
+            C = run(sd, Bd, cb, a_out=a_out, producer=producer, local_rank=local)
+            assert np.array_equal(u16(a_out), A_ref)
+            if ref is None:
+                assert_close_on_device(C, C32, producer)
+                ref = C.clone()
+            else:
+                assert torch.equal(C.view(torch.int16), ref.view(torch.int16)), (producer, local)
+    assert ag.check()[0] == ag.AG_OK
+
+
 def test_streams_and_back_to_back_calls():
     """Calls on two streams share the workspace: the library orders them, results stay right."""
     N, H, K, Nc, cb = 4, 128, 256, 256, 32
@@ -147,43 +244,29 @@ def test_streams_and_back_to_back_calls():
         assert_close_to_oracle(C, C32)
 
 
-# ------------------------------------------------------------------------------ full-size, sampled
-def sample_positions(M, Nc, H, cb, n_random=3000, seed=0):
-    rng = np.random.default_rng(seed)
-    rows = set(rng.integers(0, M, n_random // 3).tolist())
-    for b in list(range(0, M, 256)) + list(range(0, M, H)) + list(range(0, M, cb)):
-        rows.update({b, max(0, b - 1), min(M - 1, b + 1)})
-    rows.add(M - 1)
-    cols = set(rng.integers(0, Nc, 64).tolist()) | {0, 1, 255, 256, Nc - 1, Nc - 2}
-    cols = sorted(cols)
-    rows = sorted(rows)
-    ms = np.array([r for r in rows for _ in range(2)], dtype=np.int64)
-    ns = np.array([cols[(i * 7 + r) % len(cols)] for i, r in enumerate(ms)], dtype=np.int64)
-    extra_m = rng.integers(0, M, n_random)
-    extra_n = rng.integers(0, Nc, n_random)
-    return np.concatenate([ms, extra_m]), np.concatenate([ns, extra_n])
-
-
+# ------------------------------------------------------------------------------ full size
 @pytest.mark.parametrize("cfg", [workloads.AG_SQUARE, workloads.AG_MLP_UP, workloads.AG_RAGGED],
                          ids=lambda c: c.name)
-def test_full_size_workloads_sampled(cfg):
-    print("full-size %s" % cfg.name, flush=True)
+def test_full_size_workloads_every_element(cfg):
+    """The three full workloads: every element of C against the oracle; the gathered A bit for bit;
+    fused (each producer), unfused and GEMM-only C bit for bit equal."""
+    print("full-size %s: oracle" % cfg.name, flush=True)
     A, shards, B = workloads.make_ag_gemm(cfg)
+    C32 = oracle.ag_gemm_fast([u16(s) for s in shards], u16(B))
+    print("full-size %s: GPU" % cfg.name, flush=True)
     sd, Bd = to_dev(A, shards, B)
+    A_d = A.to(DEV)
     a_out = torch.full((cfg.M, cfg.K), float("nan"), dtype=torch.bfloat16, device=DEV)
     C_f = run(sd, Bd, cfg.cb, a_out=a_out)
-    assert torch.equal(a_out.view(torch.int16), A.to(DEV).view(torch.int16))   # gathered A exact
+    assert torch.equal(a_out.view(torch.int16), A_d.view(torch.int16))   # gathered A exact
+    assert_close_on_device(C_f, C32, "fused")
     C_u = run(sd, Bd, cfg.cb, mode="unfused")
-    C_g = run(sd, Bd, cfg.cb, mode="gemm_only", a_out=a_out)
     assert torch.equal(C_f.view(torch.int16), C_u.view(torch.int16))
+    C_g = run(sd, Bd, cfg.cb, mode="gemm_only", a_out=a_out)
     assert torch.equal(C_f.view(torch.int16), C_g.view(torch.int16))
+    for producer in PRODUCERS[1:]:
+        a_out.fill_(float("nan"))
+        C_p = run(sd, Bd, cfg.cb, a_out=a_out, producer=producer, local_rank=3)
+        assert torch.equal(a_out.view(torch.int16), A_d.view(torch.int16)), producer
+        assert torch.equal(C_f.view(torch.int16), C_p.view(torch.int16)), producer
     assert ag.check()[0] == ag.AG_OK
-    ms, ns = sample_positions(cfg.M, cfg.Nc, cfg.H, cfg.cb)
-    ref = oracle.ag_gemm_at([u16(s) for s in shards], u16(B), ms, ns)
-    got = C_f[torch.from_numpy(ms).to(DEV), torch.from_numpy(ns).to(DEV)].float().cpu().numpy()
-    err = np.abs(got.astype(np.float64) - ref)
-    bound = ATOL + RTOL * np.abs(ref.astype(np.float64))
-    assert not np.isnan(got).any()
-    assert (err <= bound).all(), "worst %g" % float((err - bound).max())
-    # properties that hold everywhere: finite output
-    assert torch.isfinite(C_f.float()).all()
