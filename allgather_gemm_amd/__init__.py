@@ -19,8 +19,9 @@ LIB_PATH = os.path.join(_HERE, "libaggemm.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "aggemm.h")
 
 AG_OK, AG_EINVAL, AG_ENOMEM, AG_EHIP, AG_ETIMEOUT, AG_EUNSUPPORTED = 0, -1, -2, -3, -4, -5
-MODE_FUSED, MODE_UNFUSED, MODE_GEMM_ONLY = 0, 1, 2
-_MODES = {"fused": MODE_FUSED, "unfused": MODE_UNFUSED, "gemm_only": MODE_GEMM_ONLY}
+MODE_FUSED, MODE_UNFUSED, MODE_GEMM_ONLY, MODE_PLAIN_GEMM = 0, 1, 2, 3
+_MODES = {"fused": MODE_FUSED, "unfused": MODE_UNFUSED, "gemm_only": MODE_GEMM_ONLY,
+          "plain_gemm": MODE_PLAIN_GEMM}
 PRODUCER_IN_KERNEL, PRODUCER_SIDE_STREAM, PRODUCER_COPY_ENGINE = 0, 1, 2
 _PRODUCERS = {"in_kernel": PRODUCER_IN_KERNEL, "side_stream": PRODUCER_SIDE_STREAM,
               "copy_engine": PRODUCER_COPY_ENGINE}
@@ -30,7 +31,8 @@ _i32, _i64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
 
 class AgOptions(ctypes.Structure):
     _fields_ = [("mode", _i32), ("local_rank", _i32), ("a_out", _vp), ("timeout_us", _i64),
-                ("reverse_order", _i32), ("skip_producer", _i32), ("producer", _i32)]
+                ("reverse_order", _i32), ("skip_producer", _i32), ("producer", _i32),
+                ("gemm_events", _vp * 2)]
 
 
 class AgError(RuntimeError):
@@ -106,11 +108,13 @@ def _check_dev(t: torch.Tensor, name: str):
 def ag_gemm(shards, B: torch.Tensor, comm_block_rows: int, C: torch.Tensor | None = None,
             mode: str = "fused", local_rank: int = 0, a_out: torch.Tensor | None = None,
             timeout_us: int = 0, reverse_order: bool = False, skip_producer: bool = False,
-            producer: str = "in_kernel", stream=None) -> torch.Tensor:
+            producer: str = "in_kernel", gemm_events=None, stream=None) -> torch.Tensor:
     """C (M, Nc) bf16 = concat(shards) @ B^T.  shards: N tensors (H, K) bf16; B: (Nc, K) bf16.
 
-    mode: "fused" | "unfused" | "gemm_only"; producer (fused only): "in_kernel" | "side_stream" |
-    "copy_engine".  The call is asynchronous on `stream`; check() reports a wait that gave up."""
+    mode: "fused" | "unfused" | "gemm_only" | "plain_gemm"; producer (fused only): "in_kernel" |
+    "side_stream" | "copy_engine".  gemm_events: optional (start, end) torch.cuda.Event pair that the
+    library records around the GEMM kernel's launch.  The call is asynchronous on `stream`; check()
+    reports a wait that gave up."""
     shards = list(shards)
     N = len(shards)
     if N == 0:
@@ -130,8 +134,9 @@ def ag_gemm(shards, B: torch.Tensor, comm_block_rows: int, C: torch.Tensor | Non
     _check_dev(C, "C")
     if C.dtype != torch.bfloat16 or tuple(C.shape) != (M, Nc):
         raise ValueError("C must be (M, Nc) bfloat16")
+    ev = (_vp * 2)(*(int(e.event_id) for e in gemm_events)) if gemm_events else (_vp * 2)(None, None)
     opt = AgOptions(_MODES[mode], local_rank, a_out.data_ptr() if a_out is not None else None,
-                    timeout_us, int(reverse_order), int(skip_producer), _PRODUCERS[producer])
+                    timeout_us, int(reverse_order), int(skip_producer), _PRODUCERS[producer], ev)
     if a_out is not None:
         _check_dev(a_out, "a_out")
         if a_out.dtype != torch.bfloat16 or tuple(a_out.shape) != (M, K):

@@ -143,11 +143,11 @@ int validate_gemm(const void* const* shards, int32_t N, int64_t M, int64_t K, co
     if (K > (int64_t(1) << 21))
         return AG_EUNSUPPORTED;
     if (opt) {
-        if (opt->mode < AG_MODE_FUSED || opt->mode > AG_MODE_GEMM_ONLY || opt->local_rank < 0 ||
+        if (opt->mode < AG_MODE_FUSED || opt->mode > AG_MODE_PLAIN_GEMM || opt->local_rank < 0 ||
             opt->local_rank >= N || opt->skip_producer < 0 || opt->skip_producer > 1 ||
             opt->producer < AG_PRODUCER_IN_KERNEL || opt->producer > AG_PRODUCER_COPY_ENGINE)
             return AG_EINVAL;
-        if (opt->mode == AG_MODE_GEMM_ONLY && !opt->a_out)
+        if ((opt->mode == AG_MODE_GEMM_ONLY || opt->mode == AG_MODE_PLAIN_GEMM) && !opt->a_out)
             return AG_EINVAL;
         if (opt->a_out && !aligned16(opt->a_out))
             return AG_EINVAL;
@@ -167,6 +167,17 @@ int validate_gemm(const void* const* shards, int32_t N, int64_t M, int64_t K, co
     const int64_t chunks = (int64_t)N * ((H + cb - 1) / cb);
     if (chunks > (int64_t(1) << 30))
         return AG_EUNSUPPORTED;
+    return AG_OK;
+}
+
+// Launches the GEMM kernel, bracketed by the caller's measurement events when it asked for them.
+int gemm_timed(const GemmArgs& g, GemmMode mode, const FusedPlan* f, hipStream_t s, const ag_options* opt)
+{
+    if (opt && opt->gemm_events[0])
+        AG_HIP(hipEventRecord(static_cast<hipEvent_t>(opt->gemm_events[0]), s), "hipEventRecord(gemm start)");
+    AG_HIP(launch_gemm(g, mode, f, s), "launch gemm");
+    if (opt && opt->gemm_events[1])
+        AG_HIP(hipEventRecord(static_cast<hipEvent_t>(opt->gemm_events[1]), s), "hipEventRecord(gemm end)");
     return AG_OK;
 }
 
@@ -226,7 +237,13 @@ extern "C" int ag_gemm_ex(const void* const* shards, int32_t N, int64_t M, int64
 
     if (K == 0) {
         // empty reduction: C = 0, nothing to gather
-        AG_HIP(launch_gemm(g, kGemmPlain, nullptr, s), "launch gemm");
+        if ((rc = gemm_timed(g, kGemmPlain, nullptr, s, opt)) != AG_OK)
+            return rc;
+        return end_use(*w, s);
+    }
+    if (mode == AG_MODE_PLAIN_GEMM) {
+        if ((rc = gemm_timed(g, kGemmPlain, nullptr, s, opt)) != AG_OK)
+            return rc;
         return end_use(*w, s);
     }
     if (mode == AG_MODE_UNFUSED) {
@@ -244,7 +261,8 @@ extern "C" int ag_gemm_ex(const void* const* shards, int32_t N, int64_t M, int64
         d.valid_rows = H;
         d.valid_cols = K;
         AG_HIP(launch_tgather(d, s), "launch tgather");
-        AG_HIP(launch_gemm(g, kGemmPlain, nullptr, s), "launch gemm");
+        if ((rc = gemm_timed(g, kGemmPlain, nullptr, s, opt)) != AG_OK)
+            return rc;
         return end_use(*w, s);
     }
     if ((rc = next_epoch(*w, s)) != AG_OK)
@@ -256,12 +274,14 @@ extern "C" int ag_gemm_ex(const void* const* shards, int32_t N, int64_t M, int64
         if (mode == AG_MODE_GEMM_ONLY)
             AG_HIP(launch_fill_u32(w->flags, nchunks, g.epoch, s), "fill flags");
         g.copy_pieces = kCopyNone;
-        AG_HIP(launch_gemm(g, kGemmFused, nullptr, s), "launch fused gemm");
+        if ((rc = gemm_timed(g, kGemmFused, nullptr, s, opt)) != AG_OK)
+            return rc;
     } else if (producer == AG_PRODUCER_IN_KERNEL) {
         g.copy_pieces = kCopyInKernel;
         const FusedPlan f = plan_fused(g);
         AG_HIP(launch_reset(g, f, s), "reset piece counters");
-        AG_HIP(launch_gemm(g, kGemmFused, &f, s), "launch fused gemm");
+        if ((rc = gemm_timed(g, kGemmFused, &f, s, opt)) != AG_OK)
+            return rc;
     } else if (producer == AG_PRODUCER_SIDE_STREAM) {
         // the first wave's chunks are copied by the whole GPU before the GEMM starts; the rest by a
         // copy kernel on the side stream while the GEMM runs (waiting tiles help); the call ends
@@ -274,7 +294,8 @@ extern "C" int ag_gemm_ex(const void* const* shards, int32_t N, int64_t M, int64
         AG_HIP(hipEventRecord(w->fork, s), "hipEventRecord(fork)");
         AG_HIP(hipStreamWaitEvent(w->side, w->fork, 0), "hipStreamWaitEvent(side)");
         AG_HIP(launch_producer(g, f, false, w->side), "launch producer");
-        AG_HIP(launch_gemm(g, kGemmFused, &f, s), "launch fused gemm");
+        if ((rc = gemm_timed(g, kGemmFused, &f, s, opt)) != AG_OK)
+            return rc;
         AG_HIP(hipEventRecord(w->join, w->side), "hipEventRecord(join)");
         AG_HIP(hipStreamWaitEvent(s, w->join, 0), "hipStreamWaitEvent(join)");
     } else {
@@ -283,7 +304,8 @@ extern "C" int ag_gemm_ex(const void* const* shards, int32_t N, int64_t M, int64
         g.copy_pieces = kCopyNone;
         AG_HIP(hipEventRecord(w->fork, s), "hipEventRecord(fork)");
         AG_HIP(hipStreamWaitEvent(w->side, w->fork, 0), "hipStreamWaitEvent(side)");
-        AG_HIP(launch_gemm(g, kGemmFused, nullptr, s), "launch fused gemm");
+        if ((rc = gemm_timed(g, kGemmFused, nullptr, s, opt)) != AG_OK)
+            return rc;
         const PieceMap pm = pm_make(H, comm_block_rows, N, g.local_rank, K, gemm_tile_m(), 1);
         for (int64_t pos = 0; pos < pm.nchunks; ++pos) {
             const int64_t c = pm_ready_chunk(pm, pos);

@@ -3,10 +3,12 @@
 //
 // Flag protocol (fused AllGather + MatMul article, "数据搬运与细粒度同步" and
 // "wait_signal 的实现与语义"): a chunk's rows must be visible before its flag says so.  The
-// producer side drains its stores, then publishes with an agent-scope release; the consumer
-// polls with relaxed agent-scope loads and, once it sees the value it waits for, issues an
-// agent-scope acquire fence before any of its waves reads the chunk.  Agent scope is what
-// makes the data visible across the eight XCDs (separate L2s) of one MI355X.
+// copy stores its bytes write-through (they reach memory, none stays dirty in an XCD's L2) and
+// drains them before it counts; counts and flags are read-modify-write atomics at the device's
+// point of coherence, so a consumer on any of the eight XCDs (separate L2s) that sees a flag
+// finds the chunk's bytes in memory.  A consumer's own caches hold no line of a chunk before its
+// flag rises, unless rows are not whole cache lines; then it invalidates with an agent-scope
+// acquire.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -76,34 +78,52 @@ __device__ __forceinline__ void barrier_after_lds_write()
 // Every access to a word that another workgroup writes is a read-modify-write atomic: the eight
 // XCDs have separate L2s, and an RMW is resolved at the device's point of coherence, so a poll
 // can never keep returning a copy cached in the polling XCD's L2.
-__device__ __forceinline__ uint32_t flag_peek(uint32_t* f)
+//
+// Each one is issued by lane 0 of the calling wave alone (an if-then with nothing inside but the
+// atomic, result broadcast with readfirstlane): issued by all 64 lanes, an atomic becomes 64
+// operations on one address, serialised at its memory channel.  Callers are whole waves in
+// wave-uniform control flow.
+__device__ __forceinline__ bool is_lane0() { return (threadIdx.x & 63) == 0; }
+
+__device__ __forceinline__ uint32_t wave_fetch_add(uint32_t* p, uint32_t v)
 {
-    return __hip_atomic_fetch_add(f, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t r = 0;
+    if (is_lane0())
+        r = __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __builtin_amdgcn_readfirstlane(r);
 }
 
-__device__ __forceinline__ void flag_publish(uint32_t* f, uint32_t value)
+__device__ __forceinline__ uint32_t wave_fetch_or(uint32_t* p, uint32_t v)
 {
-    (void)__hip_atomic_exchange(f, value, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    uint32_t r = 0;
+    if (is_lane0())
+        r = __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return __builtin_amdgcn_readfirstlane(r);
 }
+
+__device__ __forceinline__ void wave_exchange(uint32_t* p, uint32_t v)
+{
+    if (is_lane0())
+        (void)__hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t flag_peek(uint32_t* f) { return wave_fetch_add(f, 0u); }
+
+__device__ __forceinline__ void flag_publish(uint32_t* f, uint32_t value) { wave_exchange(f, value); }
 
 __device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 
 // Status word [code, chunk, tile, epoch]: the first failure since the host last read it wins the
 // first three words (what ag_check reports); the fourth always takes the failing call's epoch, so
-// the other waits of that call -- and only of that call -- give up at once.  Called by all 64
-// lanes of one wave: lane 0 contributes the code, the others OR in zero, and the follow-up writes
-// repeat one value, so there is no one-lane branch.
+// the other waits of that call -- and only of that call -- give up at once.  Called by a whole wave.
 __device__ __forceinline__ void report_failure(uint32_t* status, uint32_t code, uint32_t chunk, uint32_t tile,
                                                uint32_t epoch)
 {
-    const uint32_t mine = (threadIdx.x & 63) == 0 ? code : 0u;
-    const uint32_t prev = __builtin_amdgcn_readfirstlane(
-        __hip_atomic_fetch_or(&status[0], mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    if (prev == 0) {
-        (void)__hip_atomic_exchange(&status[1], chunk, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        (void)__hip_atomic_exchange(&status[2], tile, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (wave_fetch_or(&status[0], code) == 0) {
+        wave_exchange(&status[1], chunk);
+        wave_exchange(&status[2], tile);
     }
-    (void)__hip_atomic_exchange(&status[3], epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    wave_exchange(&status[3], epoch);
 }
 
 }  // namespace ag

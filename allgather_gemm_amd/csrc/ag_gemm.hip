@@ -79,15 +79,41 @@ struct KParams {
     int trickle;         // running waves copy pieces in the background
 };
 
+// The copy protocol's parameters (piece map, counters, flags) are read from the kernel argument
+// segment where they are used, through a pointer the compiler cannot see through, instead of being
+// held in scalar registers for the whole kernel: held, they stay live across the K loop, spill,
+// and their reloads land in every K step.  KParams is each kernel's first argument (offset 0).
+__device__ __forceinline__ const KParams& kparams()
+{
+    typedef const __attribute__((address_space(4))) KParams* Ptr;
+    Ptr k = (Ptr)__builtin_amdgcn_kernarg_segment_ptr();
+    asm volatile("" : "+s"(k));
+    return *(const KParams*)k;
+}
+
 // --------------------------------------------------------------------------------- copy pieces
 // The single-writer steps below run on all 64 lanes of a wave (a wave-uniform branch), never on
 // one lane: a one-lane branch inside a loop that also holds barriers lets the compiler's control
-// flow structurizer peel that lane out of the loop while the other lanes keep iterating.  Counters
-// take +n from lane 0 and +0 from the others, every result is read from lane 0, and the
-// remaining writes (exchange, compare-exchange, LDS store) repeat the same value.
-__device__ __forceinline__ uint32_t lane0_n(uint32_t n) { return (threadIdx.x & 63) == 0 ? n : 0u; }
-
+// flow structurizer peel that lane out of the loop while the other lanes keep iterating.  Only the
+// atomics themselves are issued by lane 0 (ag_device.hpp), and their results are broadcast, so
+// every decision stays wave-uniform.
 __device__ __forceinline__ uint32_t uniform_u32(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Copied bytes are stored write-through at system scope ("sc0 sc1"): when this wave's store count
+// drains they have reached memory, and no L2 holds them dirty.  That is what lets a piece be
+// published by a relaxed count after the drain -- no L2 write-back fence, which on this multi-XCD
+// part writes back the whole L2 and would sit in the GEMM's K loop.
+constexpr int kWriteThrough = 1 | 16;      // cache policy bits sc0 | sc1
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void* base, int64_t bytes)
+{
+    return make_rsrc(base, (uint32_t)bytes);
+}
+
+__device__ __forceinline__ void store_wt(__amdgpu_buffer_rsrc_t r, uint32_t off, i32x4 v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kWriteThrough);
+}
 
 // Ready-order piece index -> piece (the stress mode hands pieces out back to front).
 __device__ __forceinline__ PieceSpan piece_at(const KParams& p, int64_t q)
@@ -95,20 +121,16 @@ __device__ __forceinline__ PieceSpan piece_at(const KParams& p, int64_t q)
     return pm_piece(p.pm, p.a.reverse_order ? p.npieces - 1 - q : q);
 }
 
-// One wave: n more pieces of chunk c are complete (their stores drained); the last of the chunk's
-// pieces raises its flag.  Release on the counter orders this wave's stores (and, through the
-// workgroup barrier that precedes a workgroup copy, the other waves') before the count.
+// One wave: n more pieces of chunk c are complete -- their write-through stores have drained, so
+// the bytes are in memory -- and the last of the chunk's pieces raises its flag.  The count is an
+// atomic read-modify-write at the device's point of coherence: the wave whose count completes the
+// chunk has seen every other piece's count, each made after that piece's bytes landed.
 __device__ void publish(const KParams& p, int64_t c, uint32_t n)
 {
     const GemmArgs& a = p.a;
-    const uint32_t old = uniform_u32(
-        __hip_atomic_fetch_add(&a.done[c], lane0_n(n), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT));
-    if (old + n == (uint32_t)p.pm.ppc) {
-        // the other pieces' releases are in this counter's release sequence: acquire them (once
-        // per chunk) so the flag's release below covers their bytes too
-        acquire_agent();
+    const uint32_t old = wave_fetch_add(&a.done[c], n);
+    if (old + n == (uint32_t)p.pm.ppc)
         flag_publish(&a.flags[c], a.epoch);
-    }
 }
 
 // Publishes pieces [q0, q0 + n), grouping consecutive pieces of one chunk into one count.
@@ -129,8 +151,7 @@ __device__ void publish_range(const KParams& p, int64_t q0, int64_t n)
 // piece and sets *n (0 when the counter is spent).
 __device__ __forceinline__ int64_t take(uint32_t* ctr, int64_t end, uint32_t want, int64_t* n)
 {
-    const uint32_t t = uniform_u32(
-        __hip_atomic_fetch_add(ctr, lane0_n(want), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    const uint32_t t = wave_fetch_add(ctr, want);
     const int64_t avail = end - (int64_t)t;
     *n = avail <= 0 ? 0 : (avail < (int64_t)want ? avail : (int64_t)want);
     return (int64_t)t;
@@ -144,7 +165,8 @@ __device__ void copy_pieces(const KParams& p, int64_t q0, int64_t n, int tid)
     for (int64_t q = q0; q < q0 + n; ++q) {
         const PieceSpan sp = piece_at(p, q);
         const i32x4* src = reinterpret_cast<const i32x4*>(static_cast<const char*>(p.a.shards[sp.shard]) + sp.src_off);
-        i32x4* dst = reinterpret_cast<i32x4*>(static_cast<char*>(const_cast<void*>(p.a.A)) + sp.dst_off);
+        const __amdgpu_buffer_rsrc_t dst =
+            span_rsrc(static_cast<const char*>(p.a.A) + sp.dst_off, sp.bytes);
         const int64_t units = sp.bytes / 16;
         int64_t u = tid;
         for (; u + (U - 1) * NT < units; u += U * NT) {
@@ -154,10 +176,10 @@ __device__ void copy_pieces(const KParams& p, int64_t q0, int64_t n, int tid)
                 v[i] = src[u + i * NT];
 #pragma unroll
             for (int i = 0; i < U; ++i)
-                dst[u + i * NT] = v[i];
+                store_wt(dst, (uint32_t)((u + i * NT) * 16), v[i]);
         }
         for (; u < units; u += NT)
-            dst[u] = src[u];
+            store_wt(dst, (uint32_t)(u * 16), src[u]);
     }
     wait_vmcnt0();
     __syncthreads();
@@ -239,7 +261,11 @@ __device__ void wait_rows(const KParams& p, int64_t m0, int64_t m1, int64_t tile
             }
         }
     }
-    acquire_agent();
+    // A cache line of the gathered buffer can hold bytes of two chunks only when rows are not whole
+    // 128-byte lines; then an earlier read may have cached part of this chunk before it landed, and
+    // the L2 is invalidated.  Otherwise no line of a chunk is cached before its flag rises.
+    if (p.pm.row_bytes % 128 != 0)
+        acquire_agent();
     __syncthreads();
 }
 
@@ -247,13 +273,13 @@ __device__ void wait_rows(const KParams& p, int64_t m0, int64_t m1, int64_t tile
 // Per-wave state (wave-uniform): the piece being copied, how far its loads got, the slice loaded
 // in the last step and not yet stored, and a piece whose last store went out in the last step.
 struct Trickle {
-    int64_t q;            // piece being copied, -1 none
-    int64_t bytes;        // its size
-    int64_t off;          // next byte to load
-    int64_t pend;         // byte offset of the slice held in `data`, -1 none
-    int64_t publish_q;    // piece to publish at the next step (its stores drained meanwhile)
+    int32_t chunk;        // chunk of the piece being copied, -1 none
+    int32_t bytes;        // its size
+    int32_t off;          // next byte to load
+    int32_t pend;         // byte offset of the slice held in `data`, -1 none
+    int32_t publish;      // chunk of a piece to publish at the next step (its stores drained meanwhile)
     const char* src;
-    char* dst;
+    __amdgpu_buffer_rsrc_t dst;
     i32x4 data;
     bool exhausted;
 };
@@ -267,39 +293,40 @@ __device__ __forceinline__ void trickle_take(const KParams& p, Trickle& tr)
         return;
     }
     const PieceSpan sp = piece_at(p, q);
-    tr.q = q;
-    tr.bytes = sp.bytes;
+    tr.chunk = (int32_t)sp.chunk;
+    tr.bytes = (int32_t)sp.bytes;
     tr.off = 0;
     tr.src = static_cast<const char*>(p.a.shards[sp.shard]) + sp.src_off;
-    tr.dst = static_cast<char*>(const_cast<void*>(p.a.A)) + sp.dst_off;
+    tr.dst = span_rsrc(static_cast<const char*>(p.a.A) + sp.dst_off, sp.bytes);
 }
 
 // One K step of the background copy; called by every lane of the wave right after the step's
-// barrier, when this wave's loads and stores of the previous step have drained.
-__device__ void trickle_step(const KParams& p, Trickle& tr, int lane)
+// barrier, when this wave's loads and stores of the previous step have drained.  The protocol's
+// parameters are fetched only on the rare steps that take or publish a piece.
+__device__ void trickle_step(Trickle& tr, int lane)
 {
-    if (tr.publish_q >= 0) {
-        publish(p, piece_at(p, tr.publish_q).chunk, 1);
-        tr.publish_q = -1;
+    if (tr.publish >= 0) {
+        publish(kparams(), tr.publish, 1);
+        tr.publish = -1;
     }
     if (tr.pend >= 0) {
-        const int64_t b = tr.pend + 16 * lane;
+        const int32_t b = tr.pend + 16 * lane;
         if (b < tr.bytes)
-            *reinterpret_cast<i32x4*>(tr.dst + b) = tr.data;
+            store_wt(tr.dst, (uint32_t)b, tr.data);
         if (tr.pend + SLICE >= tr.bytes) {       // that was the piece's last slice
-            tr.publish_q = tr.q;
-            tr.q = -1;
+            tr.publish = tr.chunk;
+            tr.chunk = -1;
         }
         tr.pend = -1;
     }
-    if (tr.q < 0 && !tr.exhausted)
-        trickle_take(p, tr);
-    if (tr.q >= 0) {
+    if (tr.chunk < 0 && !tr.exhausted)
+        trickle_take(kparams(), tr);
+    if (tr.chunk >= 0) {
         if (tr.bytes == 0) {                     // empty piece past a short chunk's end
-            tr.publish_q = tr.q;
-            tr.q = -1;
+            tr.publish = tr.chunk;
+            tr.chunk = -1;
         } else {
-            const int64_t b = tr.off + 16 * lane;
+            const int32_t b = tr.off + 16 * lane;
             if (b < tr.bytes)
                 tr.data = *reinterpret_cast<const i32x4*>(tr.src + b);
             tr.pend = tr.off;
@@ -315,35 +342,35 @@ __device__ void trickle_flush(const KParams& p, Trickle& tr, int lane)
     if (tr.pend >= 0) {
         const int64_t b = tr.pend + 16 * lane;
         if (b < tr.bytes)
-            *reinterpret_cast<i32x4*>(tr.dst + b) = tr.data;
+            store_wt(tr.dst, (uint32_t)b, tr.data);
         tr.pend = -1;
     }
-    if (tr.q >= 0) {
+    if (tr.chunk >= 0) {
         // the rest of the piece, four slices in flight per lane
-        for (int64_t o = tr.off; o < tr.bytes; o += 4 * SLICE) {
+        for (int32_t o = tr.off; o < tr.bytes; o += 4 * SLICE) {
             i32x4 v[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int64_t b = o + i * SLICE + 16 * lane;
+                const int32_t b = o + i * SLICE + 16 * lane;
                 if (b < tr.bytes)
                     v[i] = *reinterpret_cast<const i32x4*>(tr.src + b);
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int64_t b = o + i * SLICE + 16 * lane;
+                const int32_t b = o + i * SLICE + 16 * lane;
                 if (b < tr.bytes)
-                    *reinterpret_cast<i32x4*>(tr.dst + b) = v[i];
+                    store_wt(tr.dst, (uint32_t)b, v[i]);
             }
         }
     }
     wait_vmcnt0();
-    if (tr.publish_q >= 0) {
-        publish(p, piece_at(p, tr.publish_q).chunk, 1);
-        tr.publish_q = -1;
+    if (tr.publish >= 0) {
+        publish(p, tr.publish, 1);
+        tr.publish = -1;
     }
-    if (tr.q >= 0) {
-        publish(p, piece_at(p, tr.q).chunk, 1);
-        tr.q = -1;
+    if (tr.chunk >= 0) {
+        publish(p, tr.chunk, 1);
+        tr.chunk = -1;
     }
 }
 
@@ -420,9 +447,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(KParams p)
     bool exhausted = false;   // (wave 0) no piece left to claim in this call
     bool failed = false;      // this workgroup gave up waiting (sticky, uniform)
     Trickle tr;               // this wave's in-loop copy (wave-uniform state)
-    tr.q = -1;
+    tr.chunk = -1;
     tr.pend = -1;
-    tr.publish_q = -1;
+    tr.publish = -1;
     tr.exhausted = !(MODE == kGemmFused && p.trickle);
 
     for (int64_t t = vid; t < num_tiles; t += G) {
@@ -435,8 +462,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(KParams p)
             a_rows = m1 - tc.m0;
         } else {
             if (MODE == kGemmFused) {
-                trickle_flush(p, tr, lane);          // a piece this wave holds never waits on anything
-                wait_rows(p, tc.m0, m1, t, tid, wave0, s_cmd, exhausted, failed);
+                trickle_flush(kparams(), tr, lane);  // a piece this wave holds never waits on anything
+                wait_rows(kparams(), tc.m0, m1, t, tid, wave0, s_cmd, exhausted, failed);
             }
             a_base = static_cast<const char*>(a.A) + tc.m0 * K * 2;
             a_rows = m1 - tc.m0;
@@ -462,14 +489,22 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(KParams p)
         // resource is re-based by kb*BK elements and shrunk by as many bytes, so rows past the
         // tile's valid rows read zeros; a 16-byte chunk past K starts its offsets at the tile's full
         // byte size, at or beyond this step's resource size, so it reads zeros (no branch per lane).
+        // The 16 LDS destinations and row offsets of a stage are rebuilt from the wave's LDS offset
+        // and the row stride at every K step (one scalar op each): left to itself the compiler
+        // keeps all of them in scalar registers for the whole kernel, and with the fused
+        // schedule's state also live they spill into the K loop.
         struct Dma {
             __amdgpu_buffer_rsrc_t ra, rb;
             uint32_t va, vb;
             char *sa, *sb;
+            uint32_t lw, rs;
             bool on;
         };
         auto dma_setup = [&](bool on, int64_t kb, char* sa, char* sb) {
             Dma d;
+            d.lw = lds_wave_off;
+            d.rs = row_stride32;
+            asm volatile("" : "+s"(d.lw), "+s"(d.rs));
             const uint32_t kbyte = (uint32_t)(kb * BK * 2);
             d.ra = make_rsrc(a_base + kbyte, a_bytes - kbyte);
             d.rb = make_rsrc(b_base + kbyte, b_bytes - kbyte);
@@ -485,9 +520,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(KParams p)
             if (!d.on)
                 return;
             if (q < 8)
-                dma16(d.ra, d.sa + q * 4096 + lds_wave_off, d.va + q * row_stride32);
+                dma16(d.ra, d.sa + q * 4096 + d.lw, d.va + q * d.rs);
             else
-                dma16(d.rb, d.sb + (q - 8) * 4096 + lds_wave_off, d.vb + (q - 8) * row_stride32);
+                dma16(d.rb, d.sb + (q - 8) * 4096 + d.lw, d.vb + (q - 8) * d.rs);
         };
         auto issue_all = [&](int64_t kb, char* sa, char* sb) {
             const Dma d = dma_setup(true, kb, sa, sb);
@@ -555,7 +590,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(KParams p)
             wait_vmcnt0();
             __syncthreads();
             if (MODE == kGemmFused)
-                trickle_step(p, tr, lane);
+                trickle_step(tr, lane);
             compute(sA1, sB1, dma_setup(nk > 1, 1, sA0, sB0));
             kb = 1;
         } else if (nk > 0) {
@@ -565,12 +600,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(KParams p)
             wait_vmcnt0();
             __syncthreads();
             if (MODE == kGemmFused)
-                trickle_step(p, tr, lane);
+                trickle_step(tr, lane);
             compute(sA0, sB0, dma_setup(true, kb + 1, sA1, sB1));
             wait_vmcnt0();
             __syncthreads();
             if (MODE == kGemmFused)
-                trickle_step(p, tr, lane);
+                trickle_step(tr, lane);
             compute(sA1, sB1, dma_setup(kb + 2 < nk, kb + 2, sA0, sB0));
         }
         __syncthreads();   // all waves done with the LDS before the next tile's loads
@@ -636,10 +671,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(KParams p)
     if (MODE == kGemmFused) {
         // the gathered output needs every chunk, also those no tile waited for: before it exits,
         // the workgroup copies whatever is still unclaimed
-        trickle_flush(p, tr, lane);
-        if (p.npieces > 0) {
-            drain_pieces<8>(p, a.ticket, p.fill_end, tid, wave0, s_cmd);
-            drain_pieces<8>(p, a.ticket + 1, p.npieces, tid, wave0, s_cmd);
+        const KParams& q = kparams();
+        trickle_flush(q, tr, lane);
+        if (q.npieces > 0) {
+            drain_pieces<8>(q, q.a.ticket, q.fill_end, tid, wave0, s_cmd);
+            drain_pieces<8>(q, q.a.ticket + 1, q.npieces, tid, wave0, s_cmd);
         }
     }
 }

@@ -44,6 +44,7 @@ extern "C" {
 #define AG_MODE_FUSED      0  /* chunked copy and GEMM overlapped, per-chunk flags */
 #define AG_MODE_UNFUSED    1  /* full gather (tgather kernel), then the GEMM: the serial schedule */
 #define AG_MODE_GEMM_ONLY  2  /* the fused GEMM with every flag already raised and no copy */
+#define AG_MODE_PLAIN_GEMM 3  /* the GEMM of the serial schedule alone, on a_out (no flags at all) */
 
 /* Who copies the chunks in AG_MODE_FUSED ([AGMM] 融合后的流水线 has the copy beside the MatMul). */
 #define AG_PRODUCER_IN_KERNEL    0  /* the GEMM's workgroups: tiles that would wait copy at once, and
@@ -59,7 +60,8 @@ typedef struct ag_options {
     int32_t mode;          /* AG_MODE_* */
     int32_t local_rank;    /* shard whose rows the rotated tile walk starts at, 0..N-1 */
     void *a_out;           /* NULL, or an (M, K) bf16 device buffer that receives the gathered A.
-                              Required for AG_MODE_GEMM_ONLY, where it must already hold it. */
+                              Required for AG_MODE_GEMM_ONLY and AG_MODE_PLAIN_GEMM, where it must
+                              already hold it. */
     int64_t timeout_us;    /* give-up time of one flag wait, microseconds (<= 0: 10 s) */
     int32_t reverse_order; /* test aid: the copy claims chunks in reverse ready order */
     int32_t skip_producer; /* test aid (AG_MODE_FUSED): copy nothing and leave the flags stale, so
@@ -68,6 +70,8 @@ typedef struct ag_options {
                               are unaffected (every call starts from fresh counters, and a give-up
                               only short-cuts the waits of the call that gave up). */
     int32_t producer;      /* AG_PRODUCER_* (AG_MODE_FUSED only) */
+    void *gemm_events[2];  /* measurement aid: NULL, or two hipEvent_t the call records on the GEMM
+                              kernel's stream right before and right after launching it */
 } ag_options;
 
 /*
