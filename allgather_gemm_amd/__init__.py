@@ -22,7 +22,7 @@ AG_OK, AG_EINVAL, AG_ENOMEM, AG_EHIP, AG_ETIMEOUT, AG_EUNSUPPORTED = 0, -1, -2, 
 MODE_FUSED, MODE_UNFUSED, MODE_GEMM_ONLY, MODE_PLAIN_GEMM = 0, 1, 2, 3
 _MODES = {"fused": MODE_FUSED, "unfused": MODE_UNFUSED, "gemm_only": MODE_GEMM_ONLY,
           "plain_gemm": MODE_PLAIN_GEMM}
-PRODUCER_IN_KERNEL, PRODUCER_SIDE_STREAM, PRODUCER_COPY_ENGINE = 0, 1, 2
+PRODUCER_SIDE_STREAM, PRODUCER_IN_KERNEL, PRODUCER_COPY_ENGINE = 0, 1, 2
 _PRODUCERS = {"in_kernel": PRODUCER_IN_KERNEL, "side_stream": PRODUCER_SIDE_STREAM,
               "copy_engine": PRODUCER_COPY_ENGINE}
 
@@ -108,11 +108,11 @@ def _check_dev(t: torch.Tensor, name: str):
 def ag_gemm(shards, B: torch.Tensor, comm_block_rows: int, C: torch.Tensor | None = None,
             mode: str = "fused", local_rank: int = 0, a_out: torch.Tensor | None = None,
             timeout_us: int = 0, reverse_order: bool = False, skip_producer: bool = False,
-            producer: str = "in_kernel", gemm_events=None, stream=None) -> torch.Tensor:
+            producer: str = "side_stream", gemm_events=None, stream=None) -> torch.Tensor:
     """C (M, Nc) bf16 = concat(shards) @ B^T.  shards: N tensors (H, K) bf16; B: (Nc, K) bf16.
 
-    mode: "fused" | "unfused" | "gemm_only" | "plain_gemm"; producer (fused only): "in_kernel" |
-    "side_stream" | "copy_engine".  gemm_events: optional (start, end) torch.cuda.Event pair that the
+    mode: "fused" | "unfused" | "gemm_only" | "plain_gemm"; producer (fused only): "side_stream" |
+    "in_kernel" | "copy_engine".  gemm_events: optional (start, end) torch.cuda.Event pair that the
     library records around the GEMM kernel's launch.  The call is asynchronous on `stream`; check()
     reports a wait that gave up."""
     shards = list(shards)

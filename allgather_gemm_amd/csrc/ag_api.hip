@@ -145,7 +145,7 @@ int validate_gemm(const void* const* shards, int32_t N, int64_t M, int64_t K, co
     if (opt) {
         if (opt->mode < AG_MODE_FUSED || opt->mode > AG_MODE_PLAIN_GEMM || opt->local_rank < 0 ||
             opt->local_rank >= N || opt->skip_producer < 0 || opt->skip_producer > 1 ||
-            opt->producer < AG_PRODUCER_IN_KERNEL || opt->producer > AG_PRODUCER_COPY_ENGINE)
+            opt->producer < AG_PRODUCER_SIDE_STREAM || opt->producer > AG_PRODUCER_COPY_ENGINE)
             return AG_EINVAL;
         if ((opt->mode == AG_MODE_GEMM_ONLY || opt->mode == AG_MODE_PLAIN_GEMM) && !opt->a_out)
             return AG_EINVAL;
@@ -268,7 +268,7 @@ extern "C" int ag_gemm_ex(const void* const* shards, int32_t N, int64_t M, int64
     if ((rc = next_epoch(*w, s)) != AG_OK)
         return rc;
     g.epoch = w->epoch;
-    const int producer = opt ? opt->producer : AG_PRODUCER_IN_KERNEL;
+    const int producer = opt ? opt->producer : AG_PRODUCER_SIDE_STREAM;
     if (mode == AG_MODE_GEMM_ONLY || (opt && opt->skip_producer)) {
         // every flag raised beforehand (GEMM-only), or none ever (test of the give-up path)
         if (mode == AG_MODE_GEMM_ONLY)

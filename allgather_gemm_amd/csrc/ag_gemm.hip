@@ -269,6 +269,22 @@ __device__ void wait_rows(const KParams& p, int64_t m0, int64_t m1, int64_t tile
     __syncthreads();
 }
 
+// Wave 0: the flags of the chunks under gathered rows [m0, m1), one per lane (lane i: the i-th
+// chunk), read in one batch -- a single round trip to the point of coherence -- while the current
+// tile computes.  Returns the lane's flag; *n is the chunk count, or -1 if there are more chunks
+// than lanes (that tile then waits the ordinary way).
+__device__ __forceinline__ uint32_t peek_rows(const KParams& p, int64_t m0, int64_t m1, int lane, int* n)
+{
+    int64_t c0, c1;
+    pm_chunks_of_rows(p.pm, m0, m1, c0, c1);
+    const int64_t cnt = c1 - c0 + 1;
+    *n = cnt > 64 ? -1 : (int)cnt;
+    uint32_t v = 0;
+    if (lane < *n)
+        v = __hip_atomic_fetch_add(&p.a.flags[c0 + lane], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return v;
+}
+
 // ------------------------------------------------------------------------- background copy
 // Per-wave state (wave-uniform): the piece being copied, how far its loads got, the slice loaded
 // in the last step and not yet stored, and a piece whose last store went out in the last step.
@@ -402,7 +418,9 @@ __device__ void drain_pieces(const KParams& p, uint32_t* ctr, int64_t end, int t
 }
 
 // ------------------------------------------------------------------------------------ GEMM
-template <int MODE>
+// TRICKLE: the running waves' background copy is compiled in (in-kernel producer only).  Idle, its
+// bookkeeping still costs a few percent of the K loop, so every other schedule runs without it.
+template <int MODE, bool TRICKLE>
 __global__ __launch_bounds__(NT, 1) void gemm_kernel(KParams p)
 {
     __shared__ __attribute__((aligned(1024))) char sA0[TILE_BYTES];
@@ -410,6 +428,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(KParams p)
     __shared__ __attribute__((aligned(1024))) char sA1[TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) char sB1[TILE_BYTES];
     __shared__ int64_t s_cmd[2];
+    __shared__ int32_t s_ready;    // wave 0's verdict on the next tile's chunks (all flags raised)
 
     const GemmArgs& a = p.a;
     const int tid = threadIdx.x;
@@ -450,7 +469,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(KParams p)
     tr.chunk = -1;
     tr.pend = -1;
     tr.publish = -1;
-    tr.exhausted = !(MODE == kGemmFused && p.trickle);
+    tr.exhausted = !(MODE == kGemmFused && TRICKLE && p.trickle);
+    // Wave 0 reads the flags of the next tile's chunks when this tile's K loop starts and judges
+    // them after its epilogue; if all were raised the next tile skips the wait (and its round
+    // trips) altogether.  Any other outcome takes the ordinary wait.
+    uint32_t peek = 0;
+    int peek_n = -1;
 
     for (int64_t t = vid; t < num_tiles; t += G) {
         const TileCoord tc = tile_of(t, p.num_pid_m, p.num_pid_n, p.pivot);
@@ -462,11 +486,26 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(KParams p)
             a_rows = m1 - tc.m0;
         } else {
             if (MODE == kGemmFused) {
-                trickle_flush(kparams(), tr, lane);  // a piece this wave holds never waits on anything
-                wait_rows(kparams(), tc.m0, m1, t, tid, wave0, s_cmd, exhausted, failed);
+                const bool ready = t != vid && __builtin_amdgcn_readfirstlane(s_ready) != 0;
+                if (!ready) {
+                    trickle_flush(kparams(), tr, lane);  // a piece this wave holds never waits on anything
+                    wait_rows(kparams(), tc.m0, m1, t, tid, wave0, s_cmd, exhausted, failed);
+                } else if (kparams().pm.row_bytes % 128 != 0) {
+                    acquire_agent();     // as at the end of an ordinary wait
+                }
             }
             a_base = static_cast<const char*>(a.A) + tc.m0 * K * 2;
             a_rows = m1 - tc.m0;
+        }
+        if (MODE == kGemmFused && wave0) {
+            peek_n = -1;
+            const int64_t tn = t + G;
+            if (tn < num_tiles) {
+                const TileCoord nc = tile_of(tn, p.num_pid_m, p.num_pid_n, p.pivot);
+                const int64_t nm1 = min(nc.m0 + BM, a.M);
+                if (!(nc.m0 >= lo && nm1 <= hi))
+                    peek = peek_rows(kparams(), nc.m0, nm1, lane, &peek_n);
+            }
         }
         const int64_t b_rows = min((int64_t)BN, a.Nc - tc.n0);
         const char* b_base = static_cast<const char*>(a.B) + tc.n0 * K * 2;
@@ -589,7 +628,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(KParams p)
             issue_all(0, sA1, sB1);
             wait_vmcnt0();
             __syncthreads();
-            if (MODE == kGemmFused)
+            if (MODE == kGemmFused && TRICKLE)
                 trickle_step(tr, lane);
             compute(sA1, sB1, dma_setup(nk > 1, 1, sA0, sB0));
             kb = 1;
@@ -599,12 +638,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(KParams p)
         for (; kb < nk; kb += 2) {
             wait_vmcnt0();
             __syncthreads();
-            if (MODE == kGemmFused)
+            if (MODE == kGemmFused && TRICKLE)
                 trickle_step(tr, lane);
             compute(sA0, sB0, dma_setup(true, kb + 1, sA1, sB1));
             wait_vmcnt0();
             __syncthreads();
-            if (MODE == kGemmFused)
+            if (MODE == kGemmFused && TRICKLE)
                 trickle_step(tr, lane);
             compute(sA1, sB1, dma_setup(kb + 2 < nk, kb + 2, sA0, sB0));
         }
@@ -666,7 +705,17 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(KParams p)
                 __builtin_amdgcn_wave_barrier();
             }
         }
-        __syncthreads();   // LDS is free again for the next tile's loads
+        if (MODE == kGemmFused) {
+            if (wave0) {
+                const bool stale = peek_n >= 0 && lane < peek_n && peek != a.epoch;
+                const bool ok = peek_n >= 0 && __builtin_amdgcn_ballot_w64(stale) == 0;
+                if (lane == 0)
+                    s_ready = ok ? 1 : 0;
+            }
+            barrier_after_lds_write();   // s_ready is visible; LDS is free for the next tile's loads
+        } else {
+            __syncthreads();   // LDS is free again for the next tile's loads
+        }
     }
     if (MODE == kGemmFused) {
         // the gathered output needs every chunk, also those no tile waited for: before it exits,
@@ -830,9 +879,12 @@ hipError_t launch_gemm(const GemmArgs& a, GemmMode mode, const FusedPlan* f, hip
         p.fill_end = f->fill_end;
     const int grid = gemm_grid(p, cus);
     if (mode == kGemmFused)
-        gemm_kernel<kGemmFused><<<grid, NT, 0, stream>>>(p);
+        if (p.trickle)
+            gemm_kernel<kGemmFused, true><<<grid, NT, 0, stream>>>(p);
+        else
+            gemm_kernel<kGemmFused, false><<<grid, NT, 0, stream>>>(p);
     else
-        gemm_kernel<kGemmPlain><<<grid, NT, 0, stream>>>(p);
+        gemm_kernel<kGemmPlain, false><<<grid, NT, 0, stream>>>(p);
     return hipGetLastError();
 }
 

@@ -1,14 +1,25 @@
 #!/usr/bin/env python3
 """Benchmark of the chunked AllGather + bf16 GEMM hot path on one MI355X.
 
-One step = one fused AG-GEMM call (chunk copy, per-chunk flags, rotated persistent MFMA GEMM) on the
-8192 x 8192 x 8192 workload: 8 shards of (1024, 8192) bf16 ~N(0,1), B (8192, 8192) bf16 ~N(0,0.02),
-comm blocks of 128 rows.  Inputs are resident in HBM before the timed region.  The JSON line also
-carries the unfused (gather, then GEMM) and GEMM-only (flags pre-raised) times of the same workload,
-the standalone TGATHER bandwidth on its two workloads, the MFMA roofline of the fused kernel, and the
-CPU oracle timed on a bounded sample.
+One step = one fused AG-GEMM call (chunk copy by a copy kernel on a second stream beside the rotated
+persistent MFMA GEMM, per-chunk flags, waiting tiles copy too) on the 8192 x 8192 x 8192 workload:
+8 shards of (1024, 8192) bf16 ~N(0,1),
+B (8192, 8192) bf16 ~N(0,0.02), comm blocks of 128 rows.  Inputs are resident in HBM before the
+timed region.  The headline is K back-to-back steps; the GEMM kernel inside them is timed with HIP
+events the library records around its launch, on its stream, which gives the roofline figure.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Besides the headline the JSON line carries, per the fused AllGather+MatMul article's reporting list
+(section 性能结果与适用边界: warm-up, statistic, baseline, effective bandwidth, utilisation):
+  * every schedule of the square workload -- fused with each producer, unfused (gather, then GEMM),
+    GEMM-only (flags raised beforehand) and the plain GEMM alone -- as median / p10 / p90 of
+    individually timed calls, cold (a 1 GiB write evicts L2 and the MALL before every call) and hot;
+  * the MLP-up (16384 x 14336 x 4096) and ragged (4000 x 28672 x 8192) workloads the same way;
+  * TGATHER on its two workloads, cold and hot, as GB/s of algorithmic traffic;
+  * the shader clock sampled while fused calls run back to back;
+  * the CPU oracle timed on a bounded sample of the square workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--reps R] [--no-cpu-baseline]
+       python bench.py --headline-only ...   (headline steps only, for kernel traces and counters)
 """
 from __future__ import annotations
 
@@ -16,47 +27,162 @@ import argparse
 import hashlib
 import json
 import os
+import re
+import shutil
+import subprocess
 import sys
+import threading
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "AG-GEMM bf16 TFLOP/s + gather GB/s (% of peak), fused vs unfused speedup"
-PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
-PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_FLOPS_PER_CLK = 256 * 4 * 1024   # CUs x SIMDs x dense bf16 flops per SIMD per clock
 PROFILES = os.path.join(ROOT, "profiles")
+GEMM_SRC = os.path.join(ROOT, "allgather_gemm_amd", "csrc", "ag_gemm.hip")
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=30,
+                    help="untimed steps first: the clock settles only after a few dozen calls")
+    ap.add_argument("--reps", type=int, default=50, help="individually timed calls per schedule statistic")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target length of the CPU sample")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="only the headline steps (plus one calibration copy): for rocprofv3 runs")
     return ap.parse_args()
 
 
-def time_calls(fn, steps, warmup, stream):
-    """Average ms per call over `steps` calls after `warmup` calls, HIP events on `stream`."""
-    import torch
+def pct(xs, q):
+    xs = sorted(xs)
+    if not xs:
+        return None
+    i = min(len(xs) - 1, max(0, int(round(q * (len(xs) - 1)))))
+    return xs[i]
+
+
+def stats(ms_list):
+    return {"median_ms": round(pct(ms_list, 0.5), 5), "p10_ms": round(pct(ms_list, 0.1), 5),
+            "p90_ms": round(pct(ms_list, 0.9), 5)}
+
+
+class Scrubber:
+    """Writes 1 GiB so that neither L2 nor the 256 MB MALL holds anything of the next call's data."""
+
+    def __init__(self, torch, dev):
+        self.buf = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        self.n = 0
+
+    def __call__(self):
+        self.n += 1
+        self.buf.fill_(float(self.n))
+
+
+def time_each(torch, fn, reps, warmup, stream, scrub=None, events=False):
+    """Individually event-timed calls.  Returns (call ms list, GEMM-kernel ms list or None)."""
     for _ in range(warmup):
-        fn()
+        fn(None)
     torch.cuda.synchronize()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(steps):
-        fn()
-    end.record(stream)
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps
+    calls, kernels = [], []
+    for _ in range(reps):
+        if scrub is not None:
+            scrub()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        k = None
+        if events:
+            k = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            k[0].record(stream)     # materialise the events before the library records them
+            k[1].record(stream)
+        e0.record(stream)
+        fn(k)
+        e1.record(stream)
+        e1.synchronize()
+        calls.append(e0.elapsed_time(e1))
+        if k is not None:
+            kernels.append(k[0].elapsed_time(k[1]))
+    return calls, (kernels if events else None)
 
 
-def recorded_traffic(tag: str, source: str):
-    """HBM bytes per launch from a committed counter summary, or None when the kernel source has
-    changed since the counters were taken."""
+class ClockSampler:
+    """Samples the GFX clock from amd-smi (or rocm-smi) in a thread while work runs."""
+
+    def __init__(self, period=0.05):
+        self.period = period
+        self.samples = []
+        self.stop_flag = False
+        self.cmd = None
+        if shutil.which("amd-smi"):
+            self.cmd = ["amd-smi", "metric", "-g", "0", "--clock", "--json"]
+        elif shutil.which("rocm-smi"):
+            self.cmd = ["rocm-smi", "-d", "0", "--showclocks", "--json"]
+
+    @staticmethod
+    def _parse(text):
+        # amd-smi: {"clock": {"gfx_0": {"clk": {"value": 2100, "unit": "MHz"}, ...}}} (layouts vary);
+        # rocm-smi: {"card0": {"sclk clock speed:": "(2100Mhz)", ...}}
+        try:
+            data = json.loads(text)
+        except ValueError:
+            return None
+        found = []
+
+        def walk(node, path):
+            if isinstance(node, dict):
+                for k, v in node.items():
+                    walk(v, path + [str(k).lower()])
+            elif isinstance(node, list):
+                for v in node:
+                    walk(v, path)
+            else:
+                p = "/".join(path)
+                if ("gfx" in p or "sclk" in p) and "min" not in p and "max" not in p and "lock" not in p.split("/")[-1]:
+                    m = re.search(r"(\d+(?:\.\d+)?)", str(node))
+                    if m and ("value" in path[-1] or "sclk" in p or path[-1] == "clk"):
+                        found.append(float(m.group(1)))
+
+        walk(data, [])
+        vals = [v for v in found if 100.0 <= v <= 5000.0]
+        return max(vals) if vals else None
+
+    def run(self):
+        while not self.stop_flag:
+            try:
+                out = subprocess.run(self.cmd, capture_output=True, text=True, timeout=5).stdout
+                v = self._parse(out)
+                if v is not None:
+                    self.samples.append(v)
+            except Exception:
+                pass
+            time.sleep(self.period)
+
+    def __enter__(self):
+        if self.cmd:
+            self.th = threading.Thread(target=self.run, daemon=True)
+            self.th.start()
+        return self
+
+    def __exit__(self, *exc):
+        self.stop_flag = True
+        if self.cmd:
+            self.th.join(timeout=10)
+
+    def result(self):
+        if not self.samples:
+            return None
+        return {"source": self.cmd[0], "samples": len(self.samples),
+                "mean_mhz": round(sum(self.samples) / len(self.samples), 1),
+                "min_mhz": min(self.samples), "max_mhz": max(self.samples)}
+
+
+def recorded_traffic(tag: str):
+    """HBM bytes per launch from a committed counter summary of the current kernel source, or None."""
     path = os.path.join(PROFILES, tag + "_counters.txt")
     if not os.path.exists(path):
         return None
@@ -65,14 +191,15 @@ def recorded_traffic(tag: str, source: str):
         if ":" in line and not line.startswith("#"):
             k, _, v = line.partition(":")
             vals[k.strip()] = v.strip()
-    sha = hashlib.sha256(open(source, "rb").read()).hexdigest()
+    sha = hashlib.sha256(open(GEMM_SRC, "rb").read()).hexdigest()
     if vals.get("kernel_source_sha256") != sha or "hbm_bytes_per_launch" not in vals:
         return None
     return float(vals["hbm_bytes_per_launch"])
 
 
-def cpu_baseline(cfg, A, shards, B, target_s):
-    """The oracle (as written, not tuned) on a bounded sample: full rows of C, all columns."""
+def cpu_baseline(cfg, shards, B, target_s):
+    """The oracle as it stands (naive ascending-k loop, gcc -O3, no -march, OpenMP) on a bounded
+    sample: full rows of C, every column."""
     import numpy as np
     import torch
     import oracle
@@ -92,13 +219,14 @@ def cpu_baseline(cfg, A, shards, B, target_s):
     flops = 2.0 * rows * cfg.Nc * cfg.K
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": "%d full rows x %d columns of C of the %s workload (%.1f s)" % (rows, cfg.Nc, cfg.name, dt)}
+            "sample": "%d full rows x %d columns of C of the %s workload (%.1f s; oracle built gcc -O3 "
+                      "-fopenmp -ffp-contract=off, no -march)" % (rows, cfg.Nc, cfg.name, dt)}
 
 
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (N shards live on one "
+        print("bench.py measures one GPU: this build has no multi-GPU path (the N shards live on one "
               "MI355X); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
@@ -110,25 +238,111 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
-    cfg = workloads.AG_SQUARE
-    A, shards, B = workloads.make_ag_gemm(cfg)
-    sd = [s.to(dev) for s in shards]
-    Bd = B.to(dev)
-    C = torch.empty((cfg.M, cfg.Nc), dtype=torch.bfloat16, device=dev)
-    a_gath = torch.empty((cfg.M, cfg.K), dtype=torch.bfloat16, device=dev)
-    torch.cuda.synchronize()
 
-    fused = lambda: ag.ag_gemm(sd, Bd, cfg.cb, C=C, a_out=a_gath)
-    ms_fused = time_calls(fused, args.steps, args.warmup, stream)
+    def load(cfg):
+        A, shards, B = workloads.make_ag_gemm(cfg)
+        sd = [s.to(dev) for s in shards]
+        Bd = B.to(dev)
+        C = torch.empty((cfg.M, cfg.Nc), dtype=torch.bfloat16, device=dev)
+        a_gath = torch.empty((cfg.M, cfg.K), dtype=torch.bfloat16, device=dev)
+        torch.cuda.synchronize()
+        return A, shards, B, sd, Bd, C, a_gath
+
+    cfg = workloads.AG_SQUARE
+    A, shards, B, sd, Bd, C, a_gath = load(cfg)
+
+    # headline: K back-to-back fused steps, the GEMM kernel of each timed by the library's events
+    kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for k in kev:
+        k[0].record(stream)
+        k[1].record(stream)
+    for _ in range(args.warmup):
+        ag.ag_gemm(sd, Bd, cfg.cb, C=C, a_out=a_gath)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(args.steps):
+        ag.ag_gemm(sd, Bd, cfg.cb, C=C, a_out=a_gath, gemm_events=kev[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_fused = start.elapsed_time(end) / args.steps
+    gemm_kernel_ms = sum(k[0].elapsed_time(k[1]) for k in kev) / args.steps
     rc, info = ag.check()
     if rc != ag.AG_OK:
         print("fused call reported %s %s" % (ag.status_str(rc), info), file=sys.stderr)
         sys.exit(1)
-    ms_unfused = time_calls(lambda: ag.ag_gemm(sd, Bd, cfg.cb, C=C, mode="unfused", a_out=a_gath),
-                            args.steps, args.warmup, stream)
-    ms_gemm_only = time_calls(lambda: ag.ag_gemm(sd, Bd, cfg.cb, C=C, mode="gemm_only", a_out=a_gath),
-                              args.steps, args.warmup, stream)
     tflops = cfg.flops / (ms_fused * 1e-3) / 1e12
+    kernel_tflops = cfg.flops / (gemm_kernel_ms * 1e-3) / 1e12
+
+    if args.headline_only:
+        # one copy of known size, for scaling the memory counters of a profiled run
+        cal = workloads.TG_FP16
+        shs = [s.to(dev) for s in workloads.make_tgather(cal.N, cal.D, cal.H, cal.W, cal.dtype, seed=cal.seed)]
+        ag.tgather(shs, cal.H, cal.W)
+        torch.cuda.synchronize()
+        print(json.dumps({"headline_only": True, "ms_per_step": round(ms_fused, 5),
+                          "gemm_kernel_ms": round(gemm_kernel_ms, 5), "TFLOP/s": round(tflops, 2),
+                          "calibration_copy_bytes_each_way": cal.payload_bytes}), flush=True)
+        return
+
+    scrub = Scrubber(torch, dev)
+    reps, warm = args.reps, 3
+
+    def schedule_stats(cfg, sd, Bd, C, a_gath, modes):
+        out = {}
+        for name, kw in modes:
+            fn = lambda k, kw=kw: ag.ag_gemm(sd, Bd, cfg.cb, C=C, a_out=a_gath, gemm_events=k, **kw)
+            cold, kcold = time_each(torch, fn, reps, warm, stream, scrub=scrub, events=True)
+            hot, khot = time_each(torch, fn, reps, warm, stream, scrub=None, events=True)
+            rc, info = ag.check()
+            if rc != ag.AG_OK:
+                print("%s reported %s %s" % (name, ag.status_str(rc), info), file=sys.stderr)
+                sys.exit(1)
+            ent = {"cold": stats(cold), "hot": stats(hot),
+                   "gemm_kernel_cold_median_ms": round(pct(kcold, 0.5), 5),
+                   "gemm_kernel_hot_median_ms": round(pct(khot, 0.5), 5)}
+            ent["cold_tflops"] = round(cfg.flops / (ent["cold"]["median_ms"] * 1e-3) / 1e12, 2)
+            ent["hot_tflops"] = round(cfg.flops / (ent["hot"]["median_ms"] * 1e-3) / 1e12, 2)
+            out[name] = ent
+        fu, un = out["fused"]["cold"]["median_ms"], out["unfused"]["cold"]["median_ms"]
+        out["fused_vs_unfused_speedup_cold"] = round(un / fu, 4)
+        out["fused_vs_unfused_speedup_hot"] = round(out["unfused"]["hot"]["median_ms"] /
+                                                    out["fused"]["hot"]["median_ms"], 4)
+        return out
+
+    modes_sq = [("fused", {}), ("fused_in_kernel", {"producer": "in_kernel"}),
+                ("fused_copy_engine", {"producer": "copy_engine"}), ("unfused", {"mode": "unfused"}),
+                ("gemm_only", {"mode": "gemm_only"}), ("plain_gemm", {"mode": "plain_gemm"})]
+    # gathered A for the GEMM-only / plain modes
+    ag.ag_gemm(sd, Bd, cfg.cb, C=C, a_out=a_gath, mode="unfused")
+    sched = schedule_stats(cfg, sd, Bd, C, a_gath, modes_sq)
+
+    # the shader clock while fused calls run back to back (about two seconds)
+    with ClockSampler() as clk:
+        t_end = time.time() + 2.0
+        while time.time() < t_end:
+            for _ in range(20):
+                ag.ag_gemm(sd, Bd, cfg.cb, C=C, a_out=a_gath)
+            torch.cuda.synchronize()
+    sclk = clk.result()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, shards, B, args.cpu_seconds)
+    del A, shards, B, sd, Bd, C, a_gath
+    torch.cuda.empty_cache()
+
+    # the other two AG-GEMM workloads
+    other = {}
+    modes_o = [("fused", {}), ("unfused", {"mode": "unfused"}), ("gemm_only", {"mode": "gemm_only"}),
+               ("plain_gemm", {"mode": "plain_gemm"})]
+    for ocfg in (workloads.AG_MLP_UP, workloads.AG_RAGGED):
+        _, _, _, osd, oBd, oC, oa = load(ocfg)
+        ag.ag_gemm(osd, oBd, ocfg.cb, C=oC, a_out=oa, mode="unfused")
+        other[ocfg.name] = schedule_stats(ocfg, osd, oBd, oC, oa, modes_o)
+        del osd, oBd, oC, oa
+        torch.cuda.empty_cache()
 
     # standalone TGATHER on its two workloads
     gathers = {}
@@ -137,17 +351,26 @@ def main():
         dst = torch.empty((tg.D[0], tg.D[1], tg.D[2], tg.N * tg.H, tg.W), dtype=tg.dtype, device=dev)
         vr = tg.valid_rows or tg.H
         vc = tg.valid_cols or tg.W
-        ms = time_calls(lambda: ag.tgather(shs, vr, vc, dst=dst), args.steps, args.warmup, stream)
-        gbs = 2.0 * tg.payload_bytes / (ms * 1e-3) / 1e9
-        gathers[tg.name] = {"ms": round(ms, 5), "GB/s": round(gbs, 1),
-                            "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4),
-                            "valid_rows": vr, "valid_cols": vc}
+        fn = lambda k: ag.tgather(shs, vr, vc, dst=dst)
+        cold, _ = time_each(torch, fn, reps, warm, stream, scrub=scrub)
+        hot, _ = time_each(torch, fn, reps, warm, stream)
+        ent = {"cold": stats(cold), "hot": stats(hot), "valid_rows": vr, "valid_cols": vc}
+        for k in ("cold", "hot"):
+            gbs = 2.0 * tg.payload_bytes / (ent[k]["median_ms"] * 1e-3) / 1e9
+            ent[k + "_GB/s"] = round(gbs, 1)
+            ent[k + "_frac_of_hbm_peak"] = round(gbs / PEAK_HBM_GBS, 4)
+        gathers[tg.name] = ent
         del shs, dst
 
-    gemm_src = os.path.join(ROOT, "allgather_gemm_amd", "csrc", "ag_gemm.hip")
-    traffic = recorded_traffic("gemm_fused_8192", gemm_src)
-    roofline = {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic}
+    traffic = recorded_traffic("gemm_fused_8192")
+    roofline = {"bound": "mfma", "achieved": round(kernel_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(kernel_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "kernel": "gemm_kernel<1, false> (fused)", "kernel_ms": round(gemm_kernel_ms, 5),
+                "flops_per_launch": cfg.flops}
+    if sclk:
+        peak_at_clock = MFMA_FLOPS_PER_CLK * sclk["mean_mhz"] * 1e6 / 1e12
+        roofline["peak_at_sampled_sclk"] = round(peak_at_clock, 1)
+        roofline["frac_at_sampled_sclk"] = round(kernel_tflops / peak_at_clock, 4)
 
     line = {
         "metric": METRIC,
@@ -163,18 +386,17 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded randn/rand, shapes of the configured workloads)",
         "config": {"workload": cfg.name + " fused", "M": cfg.M, "K": cfg.K, "Nc": cfg.Nc,
-                   "shards": cfg.N, "comm_block_rows": cfg.cb, "local_rank": 0},
+                   "shards": cfg.N, "comm_block_rows": cfg.cb, "local_rank": 0, "producer": "side_stream"},
         "roofline": roofline,
-        "schedules": {
-            "fused_ms": round(ms_fused, 5), "unfused_ms": round(ms_unfused, 5),
-            "gemm_only_ms": round(ms_gemm_only, 5),
-            "fused_vs_unfused_speedup": round(ms_unfused / ms_fused, 4),
-            "gemm_only_tflops": round(cfg.flops / (ms_gemm_only * 1e-3) / 1e12, 2),
-        },
+        "schedules": sched,
+        "workloads": other,
         "tgather": gathers,
+        "sclk": sclk,
+        "protocol": {"reps": reps, "warmup_per_statistic": warm,
+                     "cold": "1 GiB written before every timed call", "statistic": "median, p10, p90"},
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(cfg, A, shards, B, args.cpu_seconds)
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     print(json.dumps(line), flush=True)
 
 

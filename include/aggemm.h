@@ -47,10 +47,10 @@ extern "C" {
 #define AG_MODE_PLAIN_GEMM 3  /* the GEMM of the serial schedule alone, on a_out (no flags at all) */
 
 /* Who copies the chunks in AG_MODE_FUSED ([AGMM] 融合后的流水线 has the copy beside the MatMul). */
-#define AG_PRODUCER_IN_KERNEL    0  /* the GEMM's workgroups: tiles that would wait copy at once, and
-                                       every running wave copies a little per K step (default) */
-#define AG_PRODUCER_SIDE_STREAM  1  /* a copy kernel on a second stream (its first-wave part runs
-                                       before the GEMM), waiting tiles help */
+#define AG_PRODUCER_SIDE_STREAM  0  /* a copy kernel on a second stream (its first-wave part runs
+                                       before the GEMM), waiting tiles help (default) */
+#define AG_PRODUCER_IN_KERNEL    1  /* the GEMM's workgroups: tiles that would wait copy at once, and
+                                       every running wave copies a little per K step */
 #define AG_PRODUCER_COPY_ENGINE  2  /* per chunk, a device-to-device copy that uses no compute units
                                        (hipMemcpyDeviceToDeviceNoCU) then a stream write of the flag
                                        ([AGMM] 数据搬运与细粒度同步: copy, then stream_write_value32);
@@ -97,7 +97,7 @@ int ag_gemm(const void *const *shards, int32_t N, int64_t M, int64_t K, const vo
 int ag_gemm_unfused(const void *const *shards, int32_t N, int64_t M, int64_t K, const void *B,
                     int64_t Nc, void *C, int64_t comm_block_rows, void *stream);
 
-/* ag_gemm with options (NULL = defaults: fused, in-kernel producer, local_rank 0, internal buffer,
+/* ag_gemm with options (NULL = defaults: fused, side-stream producer, local_rank 0, internal buffer,
  * 10 s). */
 int ag_gemm_ex(const void *const *shards, int32_t N, int64_t M, int64_t K, const void *B,
                int64_t Nc, void *C, int64_t comm_block_rows, void *stream,
