@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
             getattr(L, name).restype = ctypes.c_int
         L.ag_gemm_ex.argtypes = gemm_args + [ctypes.POINTER(AgOptions)]
         L.ag_gemm_ex.restype = ctypes.c_int
+        L.ag_gemm_noalloc.argtypes = [_vp, _i32, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i32, _vp]
+        L.ag_gemm_noalloc.restype = ctypes.c_int
         L.tgather.argtypes = [_vp, _i32, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i32, _vp]
         L.tgather.restype = ctypes.c_int
         L.tgather_ex.argtypes = [_vp, _i32, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i64,
@@ -145,6 +147,31 @@ def ag_gemm(shards, B: torch.Tensor, comm_block_rows: int, C: torch.Tensor | Non
                           C.data_ptr(), comm_block_rows, _stream_ptr(stream), ctypes.byref(opt))
     if rc != AG_OK:
         raise AgError(rc, "ag_gemm_ex")
+    return C
+
+
+def ag_gemm_noalloc(shards, B: torch.Tensor, comm_block_rows: int, C: torch.Tensor, a_out: torch.Tensor,
+                    local_rank: int = 0, stream=None) -> torch.Tensor:
+    """ag_gemm for callers that cannot allocate: C and a_out are the caller's; the library's control
+    words are a fixed array per GPU (calls that overlap on one GPU race)."""
+    shards = list(shards)
+    N = len(shards)
+    if N == 0:
+        raise ValueError("need at least one shard")
+    H, K = shards[0].shape
+    M, Nc = N * H, B.shape[0]
+    for i, s in enumerate(shards):
+        _check_dev(s, "shard %d" % i)
+        if s.dtype != torch.bfloat16 or tuple(s.shape) != (H, K):
+            raise ValueError("shards must all be (H, K) bfloat16")
+    for t, name, shape in ((B, "B", (Nc, K)), (C, "C", (M, Nc)), (a_out, "a_out", (M, K))):
+        _check_dev(t, name)
+        if t.dtype != torch.bfloat16 or tuple(t.shape) != shape:
+            raise ValueError("%s must be %s bfloat16" % (name, shape))
+    rc = lib().ag_gemm_noalloc(ctypes.cast(_ptrs(shards), _vp), N, M, K, B.data_ptr(), Nc, C.data_ptr(),
+                               comm_block_rows, a_out.data_ptr(), local_rank, _stream_ptr(stream))
+    if rc != AG_OK:
+        raise AgError(rc, "ag_gemm_noalloc")
     return C
 
 

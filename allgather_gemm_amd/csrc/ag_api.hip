@@ -170,6 +170,40 @@ int validate_gemm(const void* const* shards, int32_t N, int64_t M, int64_t K, co
     return AG_OK;
 }
 
+// ----------------------------------------------------------------- ag_gemm_noalloc's control words
+// One fixed array per GPU: [0] fill piece counter, [1] piece counter of the rest, [4..7] status,
+// [8, 8 + max) progress flags, [8 + max, 8 + 2 max) piece counts.  Zero when the code object is
+// loaded.  Host code never uses the symbol itself (on the host it is only a stand-in): the device
+// address comes from hipGetSymbolAddress, once per device, on that device's first call.
+constexpr int64_t kNoAllocChunks = AG_NOALLOC_MAX_CHUNKS;
+constexpr int64_t kScratchWords = 8 + 2 * kNoAllocChunks;
+static __device__ __align__(256) uint32_t scratch[kScratchWords];
+
+constexpr int kMaxDevicesNoAlloc = 64;
+struct NoAllocState {
+    uint32_t* words = nullptr;   // device address of `scratch` on this device
+    uint32_t epoch = 0;          // value of a raised flag in the last call on this device
+};
+NoAllocState g_na[kMaxDevicesNoAlloc];
+
+int noalloc_state(NoAllocState** out)
+{
+    int dev = 0;
+    AG_HIP(hipGetDevice(&dev), "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevicesNoAlloc) {
+        t_err = "ag_gemm_noalloc: device index beyond the library's table";
+        return AG_EUNSUPPORTED;
+    }
+    NoAllocState& st = g_na[dev];
+    if (!st.words) {
+        void* p = nullptr;
+        AG_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+        st.words = static_cast<uint32_t*>(p);
+    }
+    *out = &st;
+    return AG_OK;
+}
+
 // Launches the GEMM kernel, bracketed by the caller's measurement events when it asked for them.
 int gemm_timed(const GemmArgs& g, GemmMode mode, const FusedPlan* f, hipStream_t s, const ag_options* opt)
 {
@@ -386,24 +420,112 @@ extern "C" int tgather(const void* const* shards, int32_t N, void* dst, int64_t 
                       elem_size, 0, stream);
 }
 
-extern "C" int ag_check(void* stream, int64_t info[4])
+extern "C" int ag_gemm_noalloc(const void* const* shards, int32_t N, int64_t M, int64_t K, const void* B,
+                               int64_t Nc, void* C, int64_t comm_block_rows, void* a_out, int32_t local_rank,
+                               void* stream)
 {
-    std::lock_guard<std::mutex> lock(g_mu);
-    Workspace* w = nullptr;
-    int rc = current_ws(&w);
-    if (rc != AG_OK)
+    ag_options o;
+    std::memset(&o, 0, sizeof o);
+    o.mode = AG_MODE_FUSED;
+    o.local_rank = local_rank;
+    o.a_out = a_out;
+    o.producer = AG_PRODUCER_IN_KERNEL;
+    int rc = validate_gemm(shards, N, M, K, B, Nc, C, comm_block_rows, &o);
+    if (rc != AG_OK || M == 0 || Nc == 0)
         return rc;
-    AG_HIP(hipStreamSynchronize(static_cast<hipStream_t>(stream)), "hipStreamSynchronize");
+    if (K > 0 && !a_out)
+        return AG_EINVAL;
+    const int64_t H = M / N;
+    const int64_t nchunks = (int64_t)N * ((H + comm_block_rows - 1) / comm_block_rows);
+    if (nchunks > kNoAllocChunks) {
+        t_err = "ag_gemm_noalloc: " + std::to_string(nchunks) + " chunks, at most " +
+                std::to_string(kNoAllocChunks);
+        return AG_EUNSUPPORTED;
+    }
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    std::lock_guard<std::mutex> lock(g_mu);
+    NoAllocState* st = nullptr;
+    if ((rc = noalloc_state(&st)) != AG_OK)
+        return rc;
+
+    GemmArgs g;
+    std::memset(&g, 0, sizeof g);
+    g.A = a_out;
+    g.B = B;
+    g.C = C;
+    g.M = M;
+    g.Nc = Nc;
+    g.K = K;
+    for (int r = 0; r < N; ++r)
+        g.shards[r] = shards[r];
+    g.nshards = N;
+    g.local_rank = local_rank;
+    g.H = H;
+    g.cb = comm_block_rows;
+    g.ticket = st->words;
+    g.status = st->words + 4;
+    g.flags = st->words + 8;
+    g.done = st->words + 8 + kNoAllocChunks;
+    g.spin_limit = (int64_t)10000000 * 100;   // 10 s of the 100 MHz clock
+    if (K == 0) {
+        AG_HIP(launch_gemm(g, kGemmPlain, nullptr, s), "launch gemm");   // C = 0
+        return AG_OK;
+    }
+    // A new flag value per call; on wrap-around the flags and the give-up word are cleared (by a
+    // kernel: no memset node if the caller captures this into a graph).
+    if (++st->epoch == 0) {
+        AG_HIP(launch_fill_u32(g.flags, kNoAllocChunks, 0u, s), "clear flags");
+        AG_HIP(launch_fill_u32(g.status + 3, 1, 0u, s), "clear give-up epoch");
+        st->epoch = 1;
+    }
+    g.epoch = st->epoch;
+    g.copy_pieces = kCopyInKernel;
+    const FusedPlan f = plan_fused(g);
+    AG_HIP(launch_reset(g, f, s), "reset piece counters");   // piece counts and counters start at 0
+    AG_HIP(launch_gemm(g, kGemmFused, &f, s), "launch gemm");
+    return AG_OK;
+}
+
+// Reads one status block; if it holds a failure, reports it and clears it.
+static int take_status(uint32_t* block, int64_t info[4], bool* failed)
+{
     uint32_t st[4] = {0, 0, 0, 0};
-    AG_HIP(hipMemcpy(st, w->ctl + 4, sizeof st, hipMemcpyDeviceToHost), "hipMemcpy(status)");
+    AG_HIP(hipMemcpy(st, block, sizeof st, hipMemcpyDeviceToHost), "hipMemcpy(status)");
+    *failed = st[0] != 0;
+    if (!*failed)
+        return AG_OK;
     if (info)
         for (int i = 0; i < 4; ++i)
             info[i] = st[i];
-    if (st[0] == 0)
-        return AG_OK;
     // the reported failure is consumed; counters need no repair (every call resets its own)
-    AG_HIP(hipMemset(w->ctl + 4, 0, 3 * sizeof(uint32_t)), "hipMemset(status)");
-    return AG_ETIMEOUT;
+    AG_HIP(hipMemset(block, 0, 3 * sizeof(uint32_t)), "hipMemset(status)");
+    return AG_OK;
+}
+
+extern "C" int ag_check(void* stream, int64_t info[4])
+{
+    std::lock_guard<std::mutex> lock(g_mu);
+    int dev = 0;
+    AG_HIP(hipGetDevice(&dev), "hipGetDevice");
+    AG_HIP(hipStreamSynchronize(static_cast<hipStream_t>(stream)), "hipStreamSynchronize");
+    if (info)
+        for (int i = 0; i < 4; ++i)
+            info[i] = 0;
+    bool failed = false;
+    int rc;
+    if (dev >= 0 && (size_t)dev < g_ws.size() && g_ws[dev].ctl) {
+        if ((rc = take_status(g_ws[dev].ctl + 4, info, &failed)) != AG_OK)
+            return rc;
+        if (failed)
+            return AG_ETIMEOUT;
+    }
+    if (dev >= 0 && dev < kMaxDevicesNoAlloc && g_na[dev].words) {
+        if ((rc = take_status(g_na[dev].words + 4, info, &failed)) != AG_OK)
+            return rc;
+        if (failed)
+            return AG_ETIMEOUT;
+    }
+    return AG_OK;
 }
 
 extern "C" const char* ag_status_str(int status)

@@ -127,9 +127,28 @@ int tgather_ex(const void *const *shards, int32_t N, void *dst, int64_t D0, int6
                int64_t D2, int64_t H, int64_t W, int64_t dst_rows, int64_t valid_rows,
                int64_t valid_cols, int32_t elem_size, int32_t root, void *stream);
 
-/* Waits for `stream`, then reads and clears the current device's status word.  Returns AG_OK,
- * or AG_ETIMEOUT with info = {code, chunk, tile, epoch} for the first flag wait that gave up since
- * the last ag_check (epoch: the failing call's flag value). */
+/* For callers that cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  The same product as ag_gemm (C, and the gathered A in
+ * a_out), by the fused schedule with the in-kernel producer on `stream` alone.  It allocates
+ * nothing and creates no stream or event: its control words (one progress flag and one piece
+ * count per chunk, two piece counters, a status block) live in a fixed array inside the library,
+ * one per GPU, held until the process ends.
+ *   a_out        (M, K) bf16 device buffer that receives the gathered A; required when K > 0
+ *   local_rank   as in ag_options, 0..N-1
+ *   other arguments as for ag_gemm.
+ * Returns AG_EUNSUPPORTED when N * ceil((M/N) / comm_block_rows) > AG_NOALLOC_MAX_CHUNKS.
+ * Every call on one GPU uses that GPU's one array: calls that overlap on one GPU (on two streams,
+ * or from two host threads without ordering) race, and the caller must order them.  A flag wait
+ * that gave up is reported by ag_check, as for the other entry points. */
+#define AG_NOALLOC_MAX_CHUNKS 32768
+int ag_gemm_noalloc(const void *const *shards, int32_t N, int64_t M, int64_t K, const void *B,
+                    int64_t Nc, void *C, int64_t comm_block_rows, void *a_out, int32_t local_rank,
+                    void *stream);
+
+/* Waits for `stream`, then reads and clears the current device's status words (the workspace's,
+ * then ag_gemm_noalloc's).  Returns AG_OK, or AG_ETIMEOUT with info = {code, chunk, tile, epoch}
+ * for the first flag wait that gave up since the last ag_check (epoch: the failing call's flag
+ * value). */
 int ag_check(void *stream, int64_t info[4]);
 
 /* Static text for a return code. */
