@@ -3,18 +3,20 @@
 //
 // Follows "CANN PTO-ISA TGATHER 指令深度解析：跨 Rank 行拼接 Gather 的实现原理与开发指南":
 //  * section 二 数学语义: dst[d0,d1,d2, r*H + i, j] = src_r[d0,d1,d2, i, j];
-//  * section 三 数据路径: data moves global -> on-chip staging tile -> global (here: HBM -> LDS
-//    by buffer-less LDS DMA, LDS -> VGPR -> HBM);
+//  * section 三 数据路径: data moves global -> on-chip staging tile -> global;
 //  * section 6.1: the outer dims D0..D2 are walked explicitly, and each rank's (H, W) plane is cut
 //    into logical tiles of valid_rows x valid_cols that slide over rows and columns, the last row
 //    and column tiles being ragged (the DYNAMIC valid-extent case); the ping/pong path overlaps the
 //    load of the next staging tile with the store of the current one;
 //  * section 7.2: rows of dst at or beyond N*H are never written; section 7.4: empty shapes move
 //    nothing.
-// A logical tile is usually far larger than LDS (e.g. 997 x 4999 fp32 is 19.9 MB), so each one is
-// moved as a sequence of sub-tiles of at most 16 KiB; the sub-tiles of all tiles of all ranks
-// and planes form one index space that a grid of workgroups walks with a stride, ping-ponging two
-// LDS buffers.  The copy is byte-exact for every element size.
+// On gfx950 the staging tile is a workgroup's registers: each logical tile is moved as a sequence
+// of sub-tiles of NT * UPT * 16 bytes, a sub-tile being loaded whole into VGPRs (16 bytes per load,
+// UPT loads per lane in flight) and then stored.  The sub-tiles of all tiles of all ranks and
+// planes form one index space that the grid walks with a stride; the load/store overlap of the
+// ping/pong scheme comes from the many workgroups resident on each CU, whose loads run while
+// others store.  An LDS hop would add traffic and buy nothing for a copy.  The copy is byte-exact
+// for every element size.
 #include "ag_device.hpp"
 #include "ag_internal.hpp"
 
@@ -24,10 +26,9 @@ namespace ag {
 namespace {
 
 constexpr int NT = 256;
-constexpr int SUB_BYTES = 16384;              // one staging buffer (ping or pong)
-constexpr int SUB_UNITS = SUB_BYTES / 16;     // 16-byte units per buffer
-constexpr int UNITS_PER_THREAD = SUB_UNITS / NT;
-constexpr int WG_PER_CU = 4;
+constexpr int UPT = 8;                        // 16-byte units per lane per sub-tile
+constexpr int SUB_BYTES = NT * UPT * 16;      // one sub-tile (32 KiB)
+constexpr int WG_PER_CU = 16;
 
 // A rectangular family of identical logical tiles inside one (rank, plane) region: the full
 // tiles, the ragged last column, the ragged last row, and the ragged corner.
@@ -49,7 +50,7 @@ struct Plan {
     int ncls;
     int64_t subs_per_region;
     int64_t total;
-    int vec;           // 1: 16-byte path through LDS; 0: element path
+    int vec;           // 1: 16-byte path; 0: element path
 };
 
 struct SubTile {
@@ -111,7 +112,8 @@ __device__ __forceinline__ Interior interior_of(const SubTile& s)
     return in;
 }
 
-// u / nu for u < 2^16, nu >= 1 (single-precision reciprocal plus one correction step)
+// u / nu for u < 2^16, nu >= 1 (single-precision reciprocal plus one correction step); a sub-tile
+// has at most NT * UPT = 2048 units.
 __device__ __forceinline__ uint32_t div_small(uint32_t u, uint32_t nu, float rcp)
 {
     uint32_t q = (uint32_t)((float)u * rcp);
@@ -122,86 +124,90 @@ __device__ __forceinline__ uint32_t div_small(uint32_t u, uint32_t nu, float rcp
     return q;
 }
 
-__device__ __forceinline__ void load_sub(const SubTile& s, const Interior& in, char* buf, int tid)
+// The sub-tile's aligned interior: all UPT loads of a lane first (all in flight at once), then the
+// stores.  Loads and stores are raw buffer operations over the sub-tile's span (under 2 GiB, which
+// the plan guarantees); a lane past the interior's end gets an offset beyond the span, where a load
+// returns zeros and a store is dropped without touching memory.  So no operation sits under a lane
+// condition, which would make the compiler wait for each load right behind it.
+constexpr int kStream = 2;            // cache policy "nt": the copy's lines are used once
+constexpr uint32_t kNowhere = 0xFFFFFFF0u;
+
+__device__ __forceinline__ void copy_interior(const SubTile& s, const Interior& in, int tid)
 {
     const uint32_t U = (uint32_t)(s.rows * in.nu);
-    const float rcp = 1.0f / (float)max<int64_t>(in.nu, 1);
-    const int wave = tid >> 6;
+    if (U == 0)
+        return;
+    const uint32_t span = (uint32_t)((s.rows - 1) * s.pitch + in.head + in.nu * 16);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(s.src, span);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(s.dst, span);
+    const uint32_t pitch = (uint32_t)s.pitch, head = (uint32_t)in.head, nu = (uint32_t)in.nu;
+    const float rcp = 1.0f / (float)nu;
+    i32x4 v[UPT];
+    uint32_t off[UPT];
 #pragma unroll
-    for (int j = 0; j < UNITS_PER_THREAD; ++j) {
+    for (int j = 0; j < UPT; ++j) {
         const uint32_t u = j * NT + tid;
-        if (u < U) {
-            const uint32_t row = div_small(u, (uint32_t)in.nu, rcp);
-            const uint32_t k = u - row * (uint32_t)in.nu;
-            const char* g = s.src + row * s.pitch + in.head + k * 16;
-            __builtin_amdgcn_global_load_lds(g, (lds_void*)(buf + (j * NT + wave * 64) * 16), 16, 0, 0);
-        }
+        const uint32_t row = div_small(u, nu, rcp);
+        off[j] = u < U ? row * pitch + head + (u - row * nu) * 16 : kNowhere;
+        v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off[j], 0, kStream);
     }
+#pragma unroll
+    for (int j = 0; j < UPT; ++j)
+        __builtin_amdgcn_raw_buffer_store_b128(v[j], rd, off[j], 0, kStream);
 }
 
-__device__ __forceinline__ void store_sub(const SubTile& s, const Interior& in, const char* buf, int tid,
-                                          int elem_size)
+// Bytes outside the aligned interior -- at most 15 at each end of a row, a whole number of elements
+// -- one element per lane: element e of the sub-tile is element e % per_row of row e / per_row,
+// counting the head's elements first.  EPT elements per lane are loaded before any is stored, so
+// the loads' latencies overlap (a narrow ragged column tile is all edge).
+template <typename T>
+__device__ __forceinline__ void copy_edges_t(const SubTile& s, const Interior& in, int tid)
 {
-    const uint32_t U = (uint32_t)(s.rows * in.nu);
-    const float rcp = 1.0f / (float)max<int64_t>(in.nu, 1);
-#pragma unroll
-    for (int j = 0; j < UNITS_PER_THREAD; ++j) {
-        const uint32_t u = j * NT + tid;
-        if (u < U) {
-            const uint32_t row = div_small(u, (uint32_t)in.nu, rcp);
-            const uint32_t k = u - row * (uint32_t)in.nu;
-            const i32x4 v = *reinterpret_cast<const i32x4*>(buf + u * 16);
-            *reinterpret_cast<i32x4*>(s.dst + row * s.pitch + in.head + k * 16) = v;
-        }
-    }
-    // bytes outside the aligned interior: at most 15 at each end of a row, copied element-wise
+    constexpr int EPT = 4;
+    const int64_t esz = sizeof(T);
+    const int64_t nh = in.head / esz;
     const int64_t tail0 = in.head + in.nu * 16;
-    if (in.head > 0 || tail0 < s.bytes) {
-        for (int64_t idx = tid; idx < 2 * s.rows; idx += NT) {
-            const int64_t row = idx >> 1;
-            const int64_t b0 = (idx & 1) ? tail0 : 0;
-            const int64_t b1 = (idx & 1) ? s.bytes : in.head;
-            const char* sp = s.src + row * s.pitch;
-            char* dp = s.dst + row * s.pitch;
-            for (int64_t b = b0; b < b1; b += elem_size) {
-                switch (elem_size) {
-                case 1: dp[b] = sp[b]; break;
-                case 2: *reinterpret_cast<uint16_t*>(dp + b) = *reinterpret_cast<const uint16_t*>(sp + b); break;
-                case 4: *reinterpret_cast<uint32_t*>(dp + b) = *reinterpret_cast<const uint32_t*>(sp + b); break;
-                default: *reinterpret_cast<uint64_t*>(dp + b) = *reinterpret_cast<const uint64_t*>(sp + b); break;
-                }
-            }
+    const int64_t per_row = nh + (s.bytes - tail0) / esz;
+    if (per_row == 0)
+        return;
+    const int64_t E = s.rows * per_row;
+    for (int64_t e0 = 0; e0 < E; e0 += (int64_t)EPT * NT) {
+        T v[EPT];
+        int64_t off[EPT];
+#pragma unroll
+        for (int j = 0; j < EPT; ++j) {
+            const int64_t e = min(e0 + j * NT + tid, E - 1);    // past the end: re-read the last one
+            const int64_t row = e / per_row, k = e - row * per_row;
+            off[j] = row * s.pitch + (k < nh ? k * esz : tail0 + (k - nh) * esz);
+            v[j] = *reinterpret_cast<const T*>(s.src + off[j]);
         }
+#pragma unroll
+        for (int j = 0; j < EPT; ++j)
+            if (e0 + j * NT + tid < E)
+                *reinterpret_cast<T*>(s.dst + off[j]) = v[j];
     }
 }
 
-// Ping/pong over the sub-tiles this workgroup owns: the LDS-DMA load of sub-tile k+1 is issued
-// before sub-tile k is stored, so the two overlap (the TgatherChunkedPingPong idea).
+__device__ __forceinline__ void copy_edges(const SubTile& s, const Interior& in, int tid, int elem_size)
+{
+    if (in.head == 0 && in.head + in.nu * 16 >= s.bytes)
+        return;
+    switch (elem_size) {
+    case 1: copy_edges_t<uint8_t>(s, in, tid); break;
+    case 2: copy_edges_t<uint16_t>(s, in, tid); break;
+    case 4: copy_edges_t<uint32_t>(s, in, tid); break;
+    default: copy_edges_t<uint64_t>(s, in, tid); break;
+    }
+}
+
 __global__ __launch_bounds__(NT) void tgather_vec_kernel(Plan P)
 {
-    __shared__ __attribute__((aligned(16))) char buf[2][SUB_BYTES];
     const int tid = threadIdx.x;
-    const int64_t G = gridDim.x;
-    int64_t q = blockIdx.x;
-    if (q >= P.total)
-        return;
-    SubTile cur = locate(P, q);
-    Interior cin = interior_of(cur);
-    load_sub(cur, cin, buf[0], tid);
-    for (int k = 0; q < P.total; ++k, q += G) {
-        wait_vmcnt0();
-        __syncthreads();           // buf[k&1] holds sub-tile q; buf[(k+1)&1] is free
-        const int64_t qn = q + G;
-        SubTile nxt;
-        Interior nin;
-        if (qn < P.total) {
-            nxt = locate(P, qn);
-            nin = interior_of(nxt);
-            load_sub(nxt, nin, buf[(k + 1) & 1], tid);
-        }
-        store_sub(cur, cin, buf[k & 1], tid, P.d.elem_size);
-        cur = nxt;
-        cin = nin;
+    for (int64_t q = blockIdx.x; q < P.total; q += gridDim.x) {
+        const SubTile s = locate(P, q);
+        const Interior in = interior_of(s);
+        copy_interior(s, in, tid);
+        copy_edges(s, in, tid, P.d.elem_size);
     }
 }
 
@@ -247,6 +253,9 @@ void add_class(Plan& P, int64_t count, int64_t ncols, int64_t row0, int64_t col0
         c.scn = 1;
         c.scw = tw;
         c.sr = std::max<int64_t>(1, std::min<int64_t>(th, SUB_BYTES / twb));
+        // a sub-tile's span, (sr - 1) * pitch + row bytes, stays under 2 GiB (32-bit buffer offsets)
+        const int64_t pitch = P.d.W * esz;
+        c.sr = std::max<int64_t>(1, std::min<int64_t>(c.sr, ((int64_t(1) << 31) - 1 - twb) / pitch + 1));
     } else {
         c.sr = 1;
         const int64_t pieces = (twb + SUB_BYTES - 1) / SUB_BYTES;

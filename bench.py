@@ -73,15 +73,17 @@ def stats(ms_list):
 
 
 class Scrubber:
-    """Writes 1 GiB so that neither L2 nor the 256 MB MALL holds anything of the next call's data."""
+    """Reads 1 GiB so that neither L2 nor the 256 MB MALL holds anything of the next call's data.
+    Reading (not writing) leaves no dirty lines behind, whose write-back would otherwise land inside
+    the timed call; the last call's own dirty lines are written back during the scrub."""
 
     def __init__(self, torch, dev):
-        self.buf = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-        self.n = 0
+        self.buf = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        self.out = torch.empty((), dtype=torch.float32, device=dev)
+        self.torch = torch
 
     def __call__(self):
-        self.n += 1
-        self.buf.fill_(float(self.n))
+        self.torch.amax(self.buf, dim=0, out=self.out)
 
 
 def time_each(torch, fn, reps, warmup, stream, scrub=None, events=False):
