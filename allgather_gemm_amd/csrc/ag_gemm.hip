@@ -418,10 +418,11 @@ __device__ void drain_pieces(const KParams& p, uint32_t* ctr, int64_t end, int t
 }
 
 // ------------------------------------------------------------------------------------ GEMM
-// TRICKLE: the running waves' background copy is compiled in (in-kernel producer only).  Idle, its
-// bookkeeping still costs a few percent of the K loop, so every other schedule runs without it.
+// The GEMM itself; MODE plain or fused.  TRICKLE: the running waves' background copy is compiled in
+// (in-kernel producer only).  Idle, its bookkeeping still costs a few percent of the K loop, so
+// every other schedule runs without it.
 template <int MODE, bool TRICKLE>
-__global__ __launch_bounds__(NT, 1) void gemm_kernel(KParams p)
+__device__ __forceinline__ void gemm_body(KParams p)
 {
     __shared__ __attribute__((aligned(1024))) char sA0[TILE_BYTES];
     __shared__ __attribute__((aligned(1024))) char sB0[TILE_BYTES];
@@ -729,6 +730,26 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(KParams p)
     }
 }
 
+// The kernels.  KParams is each one's first (only) argument, which kparams() relies on.
+__global__ __launch_bounds__(NT, 1) void gemm_plain_kernel(KParams p)
+{
+    gemm_body<kGemmPlain, false>(p);
+}
+
+// The fused kernels run beside other work on every CU -- the side-stream copy kernel, the runtime's
+// small kernels that write the copy-engine producer's flags -- and must leave room for one wave of
+// it per SIMD: the fused kernel's VGPRs plus the copy kernel's, each rounded up to the allocation
+// granule of 8, stay within the 512 per lane (a test compiles both and checks).  Without that
+// room those kernels cannot start until the GEMM ends, while the GEMM waits for them.
+__global__ __launch_bounds__(NT, 1) void gemm_fused_kernel(KParams p)
+{
+    gemm_body<kGemmFused, false>(p);
+}
+
+__global__ __launch_bounds__(NT, 1) void gemm_fused_trickle_kernel(KParams p)
+{
+    gemm_body<kGemmFused, true>(p);
+}
 
 // Copy kernel of the side-stream schedule.  Beside the GEMM (U = 8) it is small -- no LDS tile, few
 // VGPRs -- so its workgroups fit next to the GEMM's; alone on the GPU, for the pipeline fill
@@ -880,11 +901,11 @@ hipError_t launch_gemm(const GemmArgs& a, GemmMode mode, const FusedPlan* f, hip
     const int grid = gemm_grid(p, cus);
     if (mode == kGemmFused)
         if (p.trickle)
-            gemm_kernel<kGemmFused, true><<<grid, NT, 0, stream>>>(p);
+            gemm_fused_trickle_kernel<<<grid, NT, 0, stream>>>(p);
         else
-            gemm_kernel<kGemmFused, false><<<grid, NT, 0, stream>>>(p);
+            gemm_fused_kernel<<<grid, NT, 0, stream>>>(p);
     else
-        gemm_kernel<kGemmPlain, false><<<grid, NT, 0, stream>>>(p);
+        gemm_plain_kernel<<<grid, NT, 0, stream>>>(p);
     return hipGetLastError();
 }
 

@@ -367,7 +367,7 @@ def main():
     traffic = recorded_traffic("gemm_fused_8192")
     roofline = {"bound": "mfma", "achieved": round(kernel_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(kernel_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                "kernel": "gemm_kernel<1, false> (fused)", "kernel_ms": round(gemm_kernel_ms, 5),
+                "kernel": "gemm_fused_kernel", "kernel_ms": round(gemm_kernel_ms, 5),
                 "flops_per_launch": cfg.flops}
     if sclk:
         peak_at_clock = MFMA_FLOPS_PER_CLK * sclk["mean_mhz"] * 1e6 / 1e12

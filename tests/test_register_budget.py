@@ -1,0 +1,45 @@
+"""The fused GEMM kernels run next to the side-stream copy kernel (and, with the copy-engine producer,
+next to the runtime's small flag-writing kernels) on every CU, one wave of each per SIMD.  That only
+works if their VGPRs fit in one SIMD's 512 per lane together; if they do not, the copy cannot start
+while the GEMM waits for it, and every wait runs into its time-out.  This compiles the kernel source
+for gfx950 (no GPU needed) and checks the budget from the compiler's own kernel metadata."""
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "allgather_gemm_amd", "csrc", "ag_gemm.hip")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+GRANULE = 8          # VGPR allocation granule per wave (gfx950, wave64)
+VGPRS_PER_LANE = 512
+
+
+def kernel_vgprs(tmp_path):
+    out = tmp_path / "ag_gemm.s"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "--cuda-device-only", "-S", SRC,
+           "-o", str(out)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    text = out.read_text()
+    vg = {}
+    for block in text.split("  - .agpr_count")[1:]:
+        name = re.search(r"\.name:\s+(\S+)", block).group(1)
+        vg[name] = int(re.search(r"\.vgpr_count:\s+(\d+)", block).group(1))
+    return vg
+
+
+def alloc(v):
+    return (v + GRANULE - 1) // GRANULE * GRANULE
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
+def test_fused_gemm_and_concurrent_copy_kernel_fit_on_one_simd(tmp_path):
+    vg = kernel_vgprs(tmp_path)
+    fused = {n: v for n, v in vg.items() if "gemm_fused" in n}
+    copy = [v for n, v in vg.items() if "producer_kernelILi8E" in n]
+    assert len(fused) == 2 and len(copy) == 1, sorted(vg)
+    for name, v in fused.items():
+        assert alloc(v) + alloc(copy[0]) <= VGPRS_PER_LANE, (name, v, copy[0])
