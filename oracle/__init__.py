@@ -30,7 +30,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_SO):
         tmp = _SO + ".tmp%d" % os.getpid()
         cmd = ["gcc", "-O3", "-fopenmp", "-ffp-contract=off", "-fno-fast-math", "-std=c11",
-               "-Wall", "-Wextra", "-shared", "-fPIC", _SRC, "-o", tmp]
+               "-Wall", "-Wextra", "-shared", "-fPIC", _SRC, "-o", tmp, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _SO)
     return _SO
@@ -46,6 +46,10 @@ def lib() -> ctypes.CDLL:
         L.oracle_bf16_to_f32.restype = ctypes.c_float
         L.oracle_f32_to_bf16_rne.argtypes = [ctypes.c_float]
         L.oracle_f32_to_bf16_rne.restype = ctypes.c_uint16
+        L.oracle_f32_to_e4m3fn.argtypes = [ctypes.c_float]
+        L.oracle_f32_to_e4m3fn.restype = ctypes.c_uint8
+        L.oracle_e4m3fn_value.argtypes = [ctypes.c_uint8]
+        L.oracle_e4m3fn_value.restype = ctypes.c_double
         L.oracle_tgather.argtypes = [_vp, ctypes.c_int, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
                                      ctypes.c_int]
         L.oracle_tgather.restype = ctypes.c_int
@@ -95,6 +99,20 @@ def bf16_to_f32(bits: int) -> float:
 
 def f32_to_bf16_rne(x: float) -> int:
     return int(lib().oracle_f32_to_bf16_rne(x))
+
+
+def f32_to_e4m3fn(x) -> np.ndarray:
+    """E4M3 "fn" codes (uint8) of fp32 values, element by element (see oracle.h)."""
+    xs = np.asarray(x, dtype=np.float32)
+    f = lib().oracle_f32_to_e4m3fn
+    return np.array([f(float(v)) for v in xs.ravel()], dtype=np.uint8).reshape(xs.shape)
+
+
+def e4m3fn_value(codes) -> np.ndarray:
+    """Values (float64) of E4M3 "fn" codes."""
+    cs = np.asarray(codes, dtype=np.uint8)
+    f = lib().oracle_e4m3fn_value
+    return np.array([f(int(c)) for c in cs.ravel()], dtype=np.float64).reshape(cs.shape)
 
 
 def tgather(shards, dst: np.ndarray, D0: int, D1: int, D2: int, H: int, W: int,

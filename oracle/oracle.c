@@ -13,6 +13,7 @@
  */
 #include "oracle.h"
 
+#include <math.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -33,6 +34,57 @@ uint16_t oracle_f32_to_bf16_rne(float f)
     uint32_t lsb = (u >> 16) & 1u;                         /* ties go to the even result */
     u += 0x7fffu + lsb;
     return (uint16_t)(u >> 16);
+}
+
+/* E4M3 "fn" from the format's definition (see oracle.h).  Works in doubles: |x| divided by the
+ * spacing of its binade is exact, so the rounding below is exact too. */
+static double round_half_even(double v)      /* v >= 0 */
+{
+    double f = floor(v);
+    double r = v - f;
+    if (r > 0.5)
+        return f + 1.0;
+    if (r < 0.5)
+        return f;
+    return fmod(f, 2.0) == 0.0 ? f : f + 1.0;
+}
+
+uint8_t oracle_f32_to_e4m3fn(float x)
+{
+    const uint8_t sign = signbit(x) ? 0x80u : 0u;
+    if (isnan(x) || isinf(x))
+        return (uint8_t)(sign | 0x7fu);
+    const double a = fabs((double)x);
+    const double min_normal = ldexp(1.0, -6);
+    if (a < min_normal) {
+        /* subnormal binade: steps of 2^-9; 8 steps is the smallest normal, code 0x08 */
+        const double q = round_half_even(a / ldexp(1.0, -9));
+        return (uint8_t)(sign | (uint8_t)q);
+    }
+    int e2;
+    (void)frexp(a, &e2);                 /* a = f * 2^e2, f in [0.5, 1) */
+    int e = e2 - 1;                      /* a in [2^e, 2^(e+1)) */
+    double q = round_half_even(a / ldexp(1.0, e - 3));   /* 8 .. 16 steps of 2^(e-3) */
+    if (q == 16.0) {                     /* rounded up into the next binade */
+        e += 1;
+        q = 8.0;
+    }
+    const int field = e + 7;
+    const int mant = (int)q - 8;
+    if (field > 15 || (field == 15 && mant == 7))
+        return (uint8_t)(sign | 0x7fu);  /* beyond 448 */
+    return (uint8_t)(sign | (uint8_t)(field << 3) | (uint8_t)mant);
+}
+
+double oracle_e4m3fn_value(uint8_t code)
+{
+    const double s = (code & 0x80u) ? -1.0 : 1.0;
+    const int field = (code >> 3) & 15, mant = code & 7;
+    if (field == 15 && mant == 7)
+        return NAN;
+    if (field == 0)
+        return s * ldexp((double)mant, -9);
+    return s * ldexp(8.0 + mant, field - 10);
 }
 
 /* [TGATH] §二 数学语义 (closed form), §7.2 内存约束 (taller dst keeps its extra rows),

@@ -30,6 +30,18 @@ float oracle_bf16_to_f32(uint16_t h);
 uint16_t oracle_f32_to_bf16_rne(float f);
 
 /*
+ * FP8 output of the fused kernel ([AGMM] MatMul 按需等待: the MatMul is launched with FP8_OUTPUT
+ * set when C's dtype is torch.float8_e4m3fn).  The conversion is that dtype's: the OCP FP8 E4M3
+ * "fn" format -- 1 sign bit, 4 exponent bits with bias 7, 3 mantissa bits, subnormals, no
+ * infinities, the single NaN pattern S.1111.111, largest finite 448 -- with round to nearest,
+ * ties to even, onto the finite values; a value whose rounding lands beyond 448 (|x| > 464, or
+ * infinite) becomes NaN, as does a NaN.  NaN results are 0x7F with the input's sign.
+ */
+uint8_t oracle_f32_to_e4m3fn(float x);
+/* The value an E4M3 "fn" code stands for (NaN for S.1111.111). */
+double oracle_e4m3fn_value(uint8_t code);
+
+/*
  * TGATHER closed form, [TGATH] §二 数学语义:
  *   dst[d0,d1,d2, r*H + i, j] = src_r[d0,d1,d2, i, j]  for r < nranks, i < H, j < W.
  * src[r] points at rank r's (D0,D1,D2,H,W) tensor, dst at a (D0,D1,D2,dst_rows,W) tensor, all

@@ -333,3 +333,58 @@ def test_pivot_poison_catches_missing_wait():
     poison = np.full((N * H, K), 0x7FC0, dtype=np.uint16)
     C = oracle.gemm_f32(poison, np_of(B_t))
     assert np.isnan(C).all()
+
+
+# ------------------------------------------------------------------- FP8 (E4M3 "fn") output
+def test_e4m3fn_hand_cases_from_the_format_definition():
+    """Values fixed by the format itself: bias 7, 3 mantissa bits, subnormal steps of 2^-9, largest
+    finite 448 (S.1111.110), S.1111.111 is NaN; round to nearest, ties to even."""
+    cases = [
+        (0.0, 0x00), (-0.0, 0x80), (1.0, 0x38), (-2.0, 0xC0), (448.0, 0x7E), (-448.0, 0xFE),
+        (2.0 ** -6, 0x08),          # smallest normal
+        (2.0 ** -9, 0x01),          # smallest subnormal
+        (7 * 2.0 ** -9, 0x07),      # largest subnormal
+        (2.0 ** -10, 0x00),         # halfway 0 .. 2^-9: tie to the even code 0
+        (3 * 2.0 ** -10, 0x02),     # halfway 2^-9 .. 2^-8: tie to mantissa 2 (even)
+        (1.0625, 0x38),             # halfway 1 .. 1.125: tie to 1.0 (mantissa 0)
+        (1.1875, 0x3A),             # halfway 1.125 .. 1.25: tie to 1.25 (mantissa 2)
+        (1.07, 0x39),               # nearer 1.125
+        (15.0 * 2.0 ** -10, 0x08),  # halfway 7*2^-9 .. 2^-6: tie to the even code 0x08
+        (464.0, 0x7E),              # halfway 448 .. 480: tie to mantissa 110 (448)
+        (464.5, 0x7F), (1e9, 0x7F), (-465.0, 0xFF),   # rounding beyond 448: NaN
+    ]
+    for x, code in cases:
+        assert oracle.f32_to_e4m3fn(np.float32(x)) == code, (x, hex(int(oracle.f32_to_e4m3fn(np.float32(x)))))
+    assert oracle.f32_to_e4m3fn(np.float32(np.inf)) == 0x7F
+    assert oracle.f32_to_e4m3fn(np.float32(-np.inf)) == 0xFF
+    assert np.isnan(oracle.e4m3fn_value(0x7F)) and np.isnan(oracle.e4m3fn_value(0xFF))
+    assert oracle.e4m3fn_value(0x7E) == 448.0 and oracle.e4m3fn_value(0x01) == 2.0 ** -9
+
+
+def test_e4m3fn_every_code_round_trips():
+    codes = np.arange(256, dtype=np.uint8)
+    vals = oracle.e4m3fn_value(codes)
+    finite = ~np.isnan(vals)
+    assert finite.sum() == 254
+    back = oracle.f32_to_e4m3fn(vals[finite].astype(np.float32))
+    assert np.array_equal(back, codes[finite])
+    # values are strictly increasing over the non-negative codes 0x00 .. 0x7E
+    assert np.all(np.diff(vals[:0x7F]) > 0)
+
+
+def test_e4m3fn_matches_torch_float8_conversion():
+    """torch's float8_e4m3fn conversion is an independent implementation of the same rounding."""
+    rng = np.random.default_rng(5)
+    codes = np.arange(256, dtype=np.uint8)
+    vals = oracle.e4m3fn_value(codes)
+    fin = np.unique(vals[~np.isnan(vals)])
+    mids = (fin[1:] + fin[:-1]) / 2
+    xs = np.concatenate([
+        fin, mids, np.nextafter(mids.astype(np.float32), np.float32(np.inf)),
+        np.nextafter(mids.astype(np.float32), np.float32(-np.inf)),
+        rng.standard_normal(4000) * 50, np.exp(rng.uniform(-25, 6.3, 4000)) * rng.choice([-1, 1], 4000),
+        [463.99, 464.0, 464.01, 479.0, 480.0, 1e6, -1e6, np.inf, -np.inf],
+    ]).astype(np.float32)
+    ours = oracle.f32_to_e4m3fn(xs)
+    theirs = torch.from_numpy(xs).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(ours, theirs), xs[ours != theirs][:10]
