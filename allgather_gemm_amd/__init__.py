@@ -23,6 +23,8 @@ MODE_FUSED, MODE_UNFUSED, MODE_GEMM_ONLY, MODE_PLAIN_GEMM = 0, 1, 2, 3
 _MODES = {"fused": MODE_FUSED, "unfused": MODE_UNFUSED, "gemm_only": MODE_GEMM_ONLY,
           "plain_gemm": MODE_PLAIN_GEMM}
 PRODUCER_SIDE_STREAM, PRODUCER_IN_KERNEL, PRODUCER_COPY_ENGINE = 0, 1, 2
+OUT_BF16, OUT_FP8_E4M3 = 0, 1
+_OUT = {"bf16": (OUT_BF16, torch.bfloat16), "fp8_e4m3": (OUT_FP8_E4M3, torch.float8_e4m3fn)}
 _PRODUCERS = {"in_kernel": PRODUCER_IN_KERNEL, "side_stream": PRODUCER_SIDE_STREAM,
               "copy_engine": PRODUCER_COPY_ENGINE}
 
@@ -32,7 +34,7 @@ _i32, _i64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
 class AgOptions(ctypes.Structure):
     _fields_ = [("mode", _i32), ("local_rank", _i32), ("a_out", _vp), ("timeout_us", _i64),
                 ("reverse_order", _i32), ("skip_producer", _i32), ("producer", _i32),
-                ("gemm_events", _vp * 2)]
+                ("gemm_events", _vp * 2), ("out_dtype", _i32), ("out_scale", ctypes.c_float)]
 
 
 class AgError(RuntimeError):
@@ -110,11 +112,13 @@ def _check_dev(t: torch.Tensor, name: str):
 def ag_gemm(shards, B: torch.Tensor, comm_block_rows: int, C: torch.Tensor | None = None,
             mode: str = "fused", local_rank: int = 0, a_out: torch.Tensor | None = None,
             timeout_us: int = 0, reverse_order: bool = False, skip_producer: bool = False,
-            producer: str = "side_stream", gemm_events=None, stream=None) -> torch.Tensor:
-    """C (M, Nc) bf16 = concat(shards) @ B^T.  shards: N tensors (H, K) bf16; B: (Nc, K) bf16.
+            producer: str = "side_stream", gemm_events=None, stream=None, out_dtype: str = "bf16",
+            out_scale: float = 1.0) -> torch.Tensor:
+    """C (M, Nc) = concat(shards) @ B^T.  shards: N tensors (H, K) bf16; B: (Nc, K) bf16.
 
     mode: "fused" | "unfused" | "gemm_only" | "plain_gemm"; producer (fused only): "side_stream" |
-    "in_kernel" | "copy_engine".  gemm_events: optional (start, end) torch.cuda.Event pair that the
+    "in_kernel" | "copy_engine".  out_dtype: "bf16" or "fp8_e4m3" (C = e4m3fn(sum * out_scale), a
+    torch.float8_e4m3fn tensor).  gemm_events: optional (start, end) torch.cuda.Event pair that the
     library records around the GEMM kernel's launch.  The call is asynchronous on `stream`; check()
     reports a wait that gave up."""
     shards = list(shards)
@@ -131,14 +135,16 @@ def ag_gemm(shards, B: torch.Tensor, comm_block_rows: int, C: torch.Tensor | Non
     _check_dev(B, "B")
     if B.dtype != torch.bfloat16 or B.shape[1] != K:
         raise ValueError("B must be (Nc, K) bfloat16")
+    out_code, out_torch = _OUT[out_dtype]
     if C is None:
-        C = torch.empty((M, Nc), dtype=torch.bfloat16, device=B.device)
+        C = torch.empty((M, Nc), dtype=out_torch, device=B.device)
     _check_dev(C, "C")
-    if C.dtype != torch.bfloat16 or tuple(C.shape) != (M, Nc):
-        raise ValueError("C must be (M, Nc) bfloat16")
+    if C.dtype != out_torch or tuple(C.shape) != (M, Nc):
+        raise ValueError("C must be (M, Nc) %s" % out_torch)
     ev = (_vp * 2)(*(int(e.event_id) for e in gemm_events)) if gemm_events else (_vp * 2)(None, None)
     opt = AgOptions(_MODES[mode], local_rank, a_out.data_ptr() if a_out is not None else None,
-                    timeout_us, int(reverse_order), int(skip_producer), _PRODUCERS[producer], ev)
+                    timeout_us, int(reverse_order), int(skip_producer), _PRODUCERS[producer], ev,
+                    out_code, float(out_scale))
     if a_out is not None:
         _check_dev(a_out, "a_out")
         if a_out.dtype != torch.bfloat16 or tuple(a_out.shape) != (M, K):

@@ -6,6 +6,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdio>
 #include <cstring>
 #include <mutex>
@@ -149,6 +150,10 @@ int validate_gemm(const void* const* shards, int32_t N, int64_t M, int64_t K, co
             return AG_EINVAL;
         if ((opt->mode == AG_MODE_GEMM_ONLY || opt->mode == AG_MODE_PLAIN_GEMM) && !opt->a_out)
             return AG_EINVAL;
+        if (opt->out_dtype != AG_OUT_BF16 && opt->out_dtype != AG_OUT_FP8_E4M3)
+            return AG_EINVAL;
+        if (!std::isfinite(opt->out_scale))
+            return AG_EINVAL;
         if (opt->a_out && !aligned16(opt->a_out))
             return AG_EINVAL;
     }
@@ -268,6 +273,8 @@ extern "C" int ag_gemm_ex(const void* const* shards, int32_t N, int64_t M, int64
     const int64_t timeout_us = (opt && opt->timeout_us > 0) ? opt->timeout_us : 10000000;
     g.spin_limit = timeout_us * 100;   // s_memrealtime runs at 100 MHz
     g.reverse_order = opt ? opt->reverse_order : 0;
+    g.out_fp8 = (opt && opt->out_dtype == AG_OUT_FP8_E4M3) ? 1 : 0;
+    g.out_scale = (opt && opt->out_scale != 0.0f) ? opt->out_scale : 1.0f;
 
     if (K == 0) {
         // empty reduction: C = 0, nothing to gather
@@ -467,6 +474,8 @@ extern "C" int ag_gemm_noalloc(const void* const* shards, int32_t N, int64_t M, 
     g.flags = st->words + 8;
     g.done = st->words + 8 + kNoAllocChunks;
     g.spin_limit = (int64_t)10000000 * 100;   // 10 s of the 100 MHz clock
+    g.out_fp8 = 0;
+    g.out_scale = 1.0f;
     if (K == 0) {
         AG_HIP(launch_gemm(g, kGemmPlain, nullptr, s), "launch gemm");   // C = 0
         return AG_OK;

@@ -656,11 +656,17 @@ __device__ __forceinline__ void gemm_body(KParams p)
         // (round to nearest even) and writes 8 consecutive columns (16 bytes) per lane, so a row
         // segment of 256 B leaves in one coalesced piece.  Slab rows are 512 B; the 16-byte unit at
         // byte b of row r sits at b ^ (r * 16), which keeps the LDS accesses (nearly) conflict-free.
+        // FP8 output (the FP8_OUTPUT variant of [AGMM] MatMul 按需等待): the 8 values, times
+        // out_scale, go through the hardware's E4M3 "fn" conversion (round to nearest even, NaN
+        // beyond 448: the conversion of torch.float8_e4m3fn) and leave as 8 bytes.
         {
             char* slab = (wave < 2 ? sA0 : sB0) + (wave & 1) * 16384;
             const int64_t wrow0 = tc.m0 + wm * 128, wcol0 = tc.n0 + wn * 128;
             const bool vec_ok = (a.Nc % 8) == 0;
+            const bool fp8 = a.out_fp8 != 0;
+            const float scale = a.out_scale;
             __bf16* C = static_cast<__bf16*>(a.C);
+            uint8_t* C8 = static_cast<uint8_t*>(a.C);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 // lane holds slab row lane%32, columns j*32 + g*8 + (lane/32)*4 + e, e = 0..3
@@ -681,6 +687,25 @@ __device__ __forceinline__ void gemm_body(KParams p)
                     const uint32_t r = pidx >> 4, c8 = (pidx & 15) * 8;
                     const f32x4 x0 = *reinterpret_cast<const f32x4*>(slab + r * 512 + ((c8 * 4) ^ (r << 4)));
                     const f32x4 x1 = *reinterpret_cast<const f32x4*>(slab + r * 512 + (((c8 + 4) * 4) ^ (r << 4)));
+                    const int64_t grow = wrow0 + i * 32 + r, gcol = wcol0 + c8;
+                    if (fp8) {
+                        // bytes 0..3 from x0, 4..7 from x1; each call fills one 16-bit half
+                        int w0 = __builtin_amdgcn_cvt_pk_fp8_f32(x0[0] * scale, x0[1] * scale, 0, false);
+                        w0 = __builtin_amdgcn_cvt_pk_fp8_f32(x0[2] * scale, x0[3] * scale, w0, true);
+                        int w1 = __builtin_amdgcn_cvt_pk_fp8_f32(x1[0] * scale, x1[1] * scale, 0, false);
+                        w1 = __builtin_amdgcn_cvt_pk_fp8_f32(x1[2] * scale, x1[3] * scale, w1, true);
+                        if (grow < a.M) {
+                            uint8_t* dstp = C8 + grow * a.Nc + gcol;
+                            if (vec_ok && gcol + 8 <= a.Nc) {
+                                *reinterpret_cast<uint2*>(dstp) = make_uint2((uint32_t)w0, (uint32_t)w1);
+                            } else {
+                                for (int e = 0; e < 8; ++e)
+                                    if (gcol + e < a.Nc)
+                                        dstp[e] = (uint8_t)(((uint32_t)(e < 4 ? w0 : w1)) >> (8 * (e & 3)));
+                            }
+                        }
+                        continue;
+                    }
                     bf16x8 o;
                     o[0] = (__bf16)x0[0];
                     o[1] = (__bf16)x0[1];
@@ -690,7 +715,6 @@ __device__ __forceinline__ void gemm_body(KParams p)
                     o[5] = (__bf16)x1[1];
                     o[6] = (__bf16)x1[2];
                     o[7] = (__bf16)x1[3];
-                    const int64_t grow = wrow0 + i * 32 + r, gcol = wcol0 + c8;
                     if (grow < a.M) {
                         __bf16* dstp = C + grow * a.Nc + gcol;
                         if (vec_ok && gcol + 8 <= a.Nc) {

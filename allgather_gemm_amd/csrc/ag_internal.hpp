@@ -52,6 +52,8 @@ struct GemmArgs {
     int copy_pieces;        // CopyBy
     int reverse_order;      // stress: hand pieces out back to front
     int64_t spin_limit;     // 100 MHz ticks of one flag wait before giving up
+    int out_fp8;            // C is FP8 E4M3 "fn" bytes (else bf16)
+    float out_scale;        // FP8 output: C = e4m3fn(acc * out_scale)
 };
 
 // Piece plan of one fused call.

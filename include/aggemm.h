@@ -56,6 +56,13 @@ extern "C" {
                                        ([AGMM] 数据搬运与细粒度同步: copy, then stream_write_value32);
                                        the GEMM only waits */
 
+/* Element type of C (ag_options.out_dtype). */
+#define AG_OUT_BF16      0    /* bf16, round to nearest even (default) */
+#define AG_OUT_FP8_E4M3  1    /* FP8 E4M3 "fn" (OCP; torch.float8_e4m3fn), one byte per element:
+                                 C = e4m3fn(acc * out_scale), the fp32 sum times the fp32 scale,
+                                 rounded to nearest even; NaN where that lands beyond +-448
+                                 ([AGMM] MatMul 按需等待: the MatMul's FP8_OUTPUT variant) */
+
 typedef struct ag_options {
     int32_t mode;          /* AG_MODE_* */
     int32_t local_rank;    /* shard whose rows the rotated tile walk starts at, 0..N-1 */
@@ -72,6 +79,9 @@ typedef struct ag_options {
     int32_t producer;      /* AG_PRODUCER_* (AG_MODE_FUSED only) */
     void *gemm_events[2];  /* measurement aid: NULL, or two hipEvent_t the call records on the GEMM
                               kernel's stream right before and right after launching it */
+    int32_t out_dtype;     /* AG_OUT_*; with AG_OUT_FP8_E4M3, C is an (M, Nc) byte array */
+    float out_scale;       /* AG_OUT_FP8_E4M3: factor applied to the fp32 sums before the
+                              conversion; 0 means 1 (must be finite) */
 } ag_options;
 
 /*

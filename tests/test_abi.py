@@ -66,7 +66,10 @@ def test_ag_gemm_ex_rejects_bad_options():
                 ag.AgOptions(0, 0, 0x40004, 0, 0, 0, 0),    # unaligned a_out
                 ag.AgOptions(0, 0, None, 0, 0, 3, 0),       # skip_producer is 0 or 1
                 ag.AgOptions(0, 0, None, 0, 0, 0, 3),       # unknown producer
-                ag.AgOptions(0, 0, None, 0, 0, 0, -1)):
+                ag.AgOptions(0, 0, None, 0, 0, 0, -1),
+                ag.AgOptions(0, 0, None, 0, 0, 0, 0, (_vp * 2)(None, None), 2, 1.0),   # unknown C type
+                ag.AgOptions(0, 0, None, 0, 0, 0, 0, (_vp * 2)(None, None), 1, float("inf")),
+                ag.AgOptions(0, 0, None, 0, 0, 0, 0, (_vp * 2)(None, None), 1, float("nan"))):
         assert L.ag_gemm_ex(ptrs, 2, 8, 8, _vp(0x20000), 8, _vp(0x30000), 4, None,
                             ctypes.byref(opt)) == ag.AG_EINVAL
 

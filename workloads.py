@@ -88,6 +88,15 @@ def make_ag_gemm_shapes(N: int, H: int, K: int, Nc: int, seed: int = 0, a_std: f
     return make_ag_gemm(cfg)
 
 
+def make_ag_gemm_integers(N: int, H: int, K: int, Nc: int, seed: int = 0, lim: int = 3):
+    """Shards and B with integer entries in [-lim, lim] (exact in bf16): with small K every partial
+    sum is an integer far below 2^24, so an fp32 sum is exact in any order.  Returns (shards, B)."""
+    g = torch.Generator().manual_seed(seed)
+    shards = [torch.randint(-lim, lim + 1, (H, K), generator=g).to(torch.bfloat16) for _ in range(N)]
+    B = torch.randint(-lim, lim + 1, (Nc, K), generator=g).to(torch.bfloat16)
+    return shards, B
+
+
 def make_tgather(N: int, D: tuple, H: int, W: int, dtype: torch.dtype, seed: int = 0,
                  bits: bool = False):
     """Returns a list of N contiguous CPU tensors of shape (D0, D1, D2, H, W)."""
