@@ -20,6 +20,7 @@ Besides the headline the JSON line carries, per the fused AllGather+MatMul artic
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--reps R] [--no-cpu-baseline]
        python bench.py --headline-only ...   (headline steps only, for kernel traces and counters)
+       python bench.py --tgather-only ...    (TGATHER workloads only, likewise)
 """
 from __future__ import annotations
 
@@ -56,6 +57,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target length of the CPU sample")
     ap.add_argument("--headline-only", action="store_true",
                     help="only the headline steps (plus one calibration copy): for rocprofv3 runs")
+    ap.add_argument("--tgather-only", action="store_true",
+                    help="only TGATHER on its two workloads, --steps calls each: for rocprofv3 runs")
     return ap.parse_args()
 
 
@@ -95,6 +98,8 @@ def time_each(torch, fn, reps, warmup, stream, scrub=None, events=False):
     for _ in range(reps):
         if scrub is not None:
             scrub()
+        # keep the GPU busy while the host enqueues the call, so host latency stays out of the window
+        torch.cuda._sleep(100000)
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         k = None
@@ -241,6 +246,28 @@ def main():
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
 
+    if args.tgather_only:
+        out = {}
+        for tg in (workloads.TG_FP16, workloads.TG_RAGGED):
+            shs = [s.to(dev) for s in workloads.make_tgather(tg.N, tg.D, tg.H, tg.W, tg.dtype, seed=tg.seed)]
+            dst = torch.empty((tg.D[0], tg.D[1], tg.D[2], tg.N * tg.H, tg.W), dtype=tg.dtype, device=dev)
+            vr, vc = tg.valid_rows or tg.H, tg.valid_cols or tg.W
+            for _ in range(args.warmup):
+                ag.tgather(shs, vr, vc, dst=dst)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(args.steps):
+                ag.tgather(shs, vr, vc, dst=dst)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / args.steps
+            out[tg.name] = {"ms_per_call": round(ms, 5), "payload_bytes": tg.payload_bytes,
+                            "GB/s": round(2 * tg.payload_bytes / (ms * 1e-3) / 1e9, 1)}
+            del shs, dst
+        print(json.dumps({"tgather_only": True, **out}), flush=True)
+        return
+
     def load(cfg):
         A, shards, B = workloads.make_ag_gemm(cfg)
         sd = [s.to(dev) for s in shards]
@@ -278,14 +305,16 @@ def main():
     kernel_tflops = cfg.flops / (gemm_kernel_ms * 1e-3) / 1e12
 
     if args.headline_only:
-        # one copy of known size, for scaling the memory counters of a profiled run
-        cal = workloads.TG_FP16
-        shs = [s.to(dev) for s in workloads.make_tgather(cal.N, cal.D, cal.H, cal.W, cal.dtype, seed=cal.seed)]
-        ag.tgather(shs, cal.H, cal.W)
+        # one copy of known size, for scaling the memory counters of a profiled run: 256 MiB read
+        # and written once each, with the caches evicted first so that every byte comes from HBM
+        shs = [torch.ones((4096, 4096), dtype=torch.float16, device=dev) for _ in range(8)]
+        dst = torch.empty((8 * 4096, 4096), dtype=torch.float16, device=dev)
+        Scrubber(torch, dev)()
+        ag.tgather(shs, 4096, 4096, dst=dst)
         torch.cuda.synchronize()
         print(json.dumps({"headline_only": True, "ms_per_step": round(ms_fused, 5),
                           "gemm_kernel_ms": round(gemm_kernel_ms, 5), "TFLOP/s": round(tflops, 2),
-                          "calibration_copy_bytes_each_way": cal.payload_bytes}), flush=True)
+                          "calibration_copy_bytes_each_way": 8 * 4096 * 4096 * 2}), flush=True)
         return
 
     scrub = Scrubber(torch, dev)
