@@ -46,6 +46,10 @@ def lib() -> ctypes.CDLL:
         L.oracle_bf16_to_f32.restype = ctypes.c_float
         L.oracle_f32_to_bf16_rne.argtypes = [ctypes.c_float]
         L.oracle_f32_to_bf16_rne.restype = ctypes.c_uint16
+        L.oracle_f32_to_bf16_array.argtypes = [_vp, _i64, _vp]
+        L.oracle_f32_to_bf16_array.restype = None
+        L.oracle_reduce_block.argtypes = [_vp, ctypes.c_int, _i64, _i64, _vp]
+        L.oracle_reduce_block.restype = None
         L.oracle_f32_to_e4m3fn.argtypes = [ctypes.c_float]
         L.oracle_f32_to_e4m3fn.restype = ctypes.c_uint8
         L.oracle_e4m3fn_value.argtypes = [ctypes.c_uint8]
@@ -99,6 +103,37 @@ def bf16_to_f32(bits: int) -> float:
 
 def f32_to_bf16_rne(x: float) -> int:
     return int(lib().oracle_f32_to_bf16_rne(x))
+
+
+def f32_to_bf16(x) -> np.ndarray:
+    """bf16 bit patterns (uint16) of fp32 values, round to nearest even."""
+    xs = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(xs.shape, dtype=np.uint16)
+    lib().oracle_f32_to_bf16_array(_ptr(xs), xs.size, _ptr(out))
+    return out
+
+
+def reduce_block(parts) -> np.ndarray:
+    """One rank's ReduceScatter block: bf16 of the fp32 sum, ascending rank, of parts (H, Nc) bf16."""
+    parts = [_as_u16(p) for p in parts]
+    H, Nc = parts[0].shape
+    out = np.empty((H, Nc), dtype=np.uint16)
+    lib().oracle_reduce_block(ctypes.cast(_ptr_array(parts), _vp), len(parts), H, Nc, _ptr(out))
+    return out
+
+
+def gemm_rs(A, B, recv, local: int):
+    """One rank's GEMM + ReduceScatter (row-parallel partial products, reduced over M blocks).
+
+    A (M, K) and B (Nc, K) bf16 are this rank's K slices; recv[j] (H, Nc) bf16, H = M / N, is rank j's
+    partial for this rank's rows (recv[local] unused).  Returns (P, out): P (M, Nc) bf16 =
+    bf16_rne(A B^T) with fp32 ascending-k sums, and out (H, Nc) bf16 = reduce_block of the N partials
+    for rows [local H, (local + 1) H), this rank's own rows of P in slot `local`."""
+    P = f32_to_bf16(gemm_f32(A, B))
+    N = len(recv)
+    H = P.shape[0] // N
+    parts = [P[local * H:(local + 1) * H] if j == local else _as_u16(recv[j]) for j in range(N)]
+    return P, reduce_block(parts)
 
 
 def f32_to_e4m3fn(x) -> np.ndarray:

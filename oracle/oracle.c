@@ -36,6 +36,23 @@ uint16_t oracle_f32_to_bf16_rne(float f)
     return (uint16_t)(u >> 16);
 }
 
+void oracle_f32_to_bf16_array(const float *x, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_f32_to_bf16_rne(x[i]);
+}
+
+/* [AGMM] 从集合通信理解数据流 (ReduceScatter: a rank keeps the reduction of its block). */
+void oracle_reduce_block(const uint16_t *const *parts, int nparts, int64_t H, int64_t Nc, uint16_t *out)
+{
+    for (int64_t i = 0; i < H * Nc; ++i) {
+        float s = 0.0f;
+        for (int j = 0; j < nparts; ++j)
+            s += oracle_bf16_to_f32(parts[j][i]);
+        out[i] = oracle_f32_to_bf16_rne(s);
+    }
+}
+
 /* E4M3 "fn" from the format's definition (see oracle.h).  Works in doubles: |x| divided by the
  * spacing of its binade is exact, so the rounding below is exact too. */
 static double round_half_even(double v)      /* v >= 0 */

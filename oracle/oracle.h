@@ -29,6 +29,17 @@ float oracle_bf16_to_f32(uint16_t h);
 /* fp32 -> bf16 bit pattern, round to nearest, ties to even; NaN stays a quiet NaN. */
 uint16_t oracle_f32_to_bf16_rne(float f);
 
+/* fp32 -> bf16 (round to nearest even) over n values. */
+void oracle_f32_to_bf16_array(const float *x, int64_t n, uint16_t *out);
+
+/*
+ * ReduceScatter of one rank's block, [AGMM] 从集合通信理解数据流: every rank keeps the reduction,
+ * over all ranks, of its own block.  parts[j] points at rank j's (H, Nc) bf16 contribution to this
+ * block; out[i, n] = bf16_rne( f32(parts[0][i, n]) + f32(parts[1][i, n]) + ... ), summed in fp32 in
+ * ascending j.
+ */
+void oracle_reduce_block(const uint16_t *const *parts, int nparts, int64_t H, int64_t Nc, uint16_t *out);
+
 /*
  * FP8 output of the fused kernel ([AGMM] MatMul 按需等待: the MatMul is launched with FP8_OUTPUT
  * set when C's dtype is torch.float8_e4m3fn).  The conversion is that dtype's: the OCP FP8 E4M3

@@ -388,3 +388,58 @@ def test_e4m3fn_matches_torch_float8_conversion():
     ours = oracle.f32_to_e4m3fn(xs)
     theirs = torch.from_numpy(xs).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     assert np.array_equal(ours, theirs), xs[ours != theirs][:10]
+
+
+# ------------------------------------------------------------------ GEMM + ReduceScatter (one rank)
+def _int_bf16(rng, shape, lim):
+    """Small integers as bf16 bit patterns (exact)."""
+    v = rng.integers(-lim, lim + 1, shape).astype(np.float32)
+    return oracle.f32_to_bf16(v), v.astype(np.int64)
+
+
+def test_reduce_scatter_then_allgather_is_allreduce():
+    """[AGMM] 从集合通信理解数据流: ReduceScatter followed by AllGather equals AllReduce.  With
+    integer-valued partials every fp32 sum is exact, so the AllReduce is computed independently in
+    int64 and the identity must hold bit for bit."""
+    rng = np.random.default_rng(11)
+    N, H, Nc = 4, 6, 40
+    parts_bits, parts_int = zip(*[_int_bf16(rng, (N * H, Nc), 50) for _ in range(N)])
+    gathered = np.concatenate([oracle.reduce_block([p[r * H:(r + 1) * H] for p in parts_bits]) for r in range(N)])
+    allreduce = oracle.f32_to_bf16(np.sum(np.stack(parts_int), axis=0).astype(np.float32))
+    assert np.array_equal(gathered, allreduce)
+
+
+def test_reduce_block_sums_in_fp32_in_ascending_rank_order():
+    """Where the fp32 order matters: 2^24 + 1 rounds back to 2^24 (a tie, to even), so in ascending
+    order 2^24, 1, 1, -2^24 sums to 0; in the reverse order the partial sums stay exact and give 2."""
+    vals = [2.0 ** 24, 1.0, 1.0, -(2.0 ** 24)]
+    parts = [oracle.f32_to_bf16(np.full((1, 8), v, dtype=np.float32)) for v in vals]
+    assert np.all(oracle.reduce_block(parts) == 0)
+    rev = oracle.reduce_block(parts[::-1])
+    assert np.all(rev == oracle.f32_to_bf16(np.float32(2.0)))
+
+
+def test_gemm_rs_exact_integers_against_int64():
+    rng = np.random.default_rng(12)
+    N, H, K, Nc = 3, 5, 24, 16
+    A_bits, A_int = _int_bf16(rng, (N * H, K), 2)
+    B_bits, B_int = _int_bf16(rng, (Nc, K), 2)
+    recv = [_int_bf16(rng, (H, Nc), 30) for _ in range(N)]
+    for local in range(N):
+        P, out = oracle.gemm_rs(A_bits, B_bits, [r[0] for r in recv], local)
+        P_int = A_int @ B_int.T
+        assert np.array_equal(P, oracle.f32_to_bf16(P_int.astype(np.float32)))
+        want = P_int[local * H:(local + 1) * H] + sum(recv[j][1] for j in range(N) if j != local)
+        assert np.array_equal(out, oracle.f32_to_bf16(want.astype(np.float32)))
+
+
+def test_reduce_block_within_rounding_of_the_exact_sum():
+    rng = np.random.default_rng(13)
+    parts = [oracle.f32_to_bf16(rng.standard_normal((7, 33)).astype(np.float32)) for _ in range(8)]
+    vals = [np.array([oracle.bf16_to_f32(int(b)) for b in p.ravel()]).reshape(p.shape) for p in parts]
+    exact = np.sum(vals, axis=0)
+    out = np.array([oracle.bf16_to_f32(int(b)) for b in oracle.reduce_block(parts).ravel()]).reshape(exact.shape)
+    # fp32 sum of 8 terms (7 roundings, each within 2^-24 relative of a partial sum), then one bf16
+    # rounding (8 significant bits: within 2^-8 relative)
+    bound = 2.0 ** -8 * np.abs(exact) + 8 * 2.0 ** -24 * np.sum(np.abs(vals), axis=0) * 1.01
+    assert np.all(np.abs(out - exact) <= bound)
