@@ -62,6 +62,8 @@ def lib() -> ctypes.CDLL:
             getattr(L, name).restype = ctypes.c_int
         L.ag_gemm_ex.argtypes = gemm_args + [ctypes.POINTER(AgOptions)]
         L.ag_gemm_ex.restype = ctypes.c_int
+        L.gemm_rs.argtypes = [_vp, _vp, _i32, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _i32, _vp]
+        L.gemm_rs.restype = ctypes.c_int
         L.ag_gemm_noalloc.argtypes = [_vp, _i32, _i64, _i64, _vp, _i64, _vp, _i64, _vp, _i32, _vp]
         L.ag_gemm_noalloc.restype = ctypes.c_int
         L.tgather.argtypes = [_vp, _i32, _vp, _i64, _i64, _i64, _i64, _i64, _i64, _i64, _i32, _vp]
@@ -179,6 +181,50 @@ def ag_gemm_noalloc(shards, B: torch.Tensor, comm_block_rows: int, C: torch.Tens
     if rc != AG_OK:
         raise AgError(rc, "ag_gemm_noalloc")
     return C
+
+
+RS_FUSED, RS_UNFUSED = 0, 1
+
+
+def gemm_rs(A: torch.Tensor, B: torch.Tensor, recv, local_rank: int, P: torch.Tensor | None = None,
+            out: torch.Tensor | None = None, fused: bool = True, stream=None):
+    """One rank's GEMM + ReduceScatter.  A (M, K), B (Nc, K) bf16: this rank's K slices; recv: N
+    tensors (H, Nc) bf16, H = M / N, the other ranks' partials for this rank's rows (recv[local_rank]
+    may be None).  Returns (P, out): P (M, Nc) = A B^T, out (H, Nc) = the reduction of this rank's
+    row block over the N partials."""
+    recv = list(recv)
+    N = len(recv)
+    M, K = A.shape
+    Nc = B.shape[0]
+    if N == 0 or M % N != 0:
+        raise ValueError("need N >= 1 partials and M % N == 0")
+    H = M // N
+    for t, name in ((A, "A"), (B, "B")):
+        _check_dev(t, name)
+        if t.dtype != torch.bfloat16:
+            raise ValueError("%s must be bfloat16" % name)
+    if B.shape[1] != K:
+        raise ValueError("B must be (Nc, K)")
+    for j, t in enumerate(recv):
+        if j == local_rank:
+            continue
+        _check_dev(t, "recv[%d]" % j)
+        if t.dtype != torch.bfloat16 or tuple(t.shape) != (H, Nc):
+            raise ValueError("recv[%d] must be (H, Nc) bfloat16" % j)
+    if P is None:
+        P = torch.empty((M, Nc), dtype=torch.bfloat16, device=A.device)
+    if out is None:
+        out = torch.empty((H, Nc), dtype=torch.bfloat16, device=A.device)
+    for t, name, shape in ((P, "P", (M, Nc)), (out, "out", (H, Nc))):
+        _check_dev(t, name)
+        if t.dtype != torch.bfloat16 or tuple(t.shape) != shape:
+            raise ValueError("%s must be %s bfloat16" % (name, shape))
+    ptrs = (_vp * N)(*[None if j == local_rank or t is None else t.data_ptr() for j, t in enumerate(recv)])
+    rc = lib().gemm_rs(A.data_ptr(), B.data_ptr(), N, local_rank, M, Nc, K, ctypes.cast(ptrs, _vp),
+                       P.data_ptr(), out.data_ptr(), RS_FUSED if fused else RS_UNFUSED, _stream_ptr(stream))
+    if rc != AG_OK:
+        raise AgError(rc, "gemm_rs")
+    return P, out
 
 
 def ag_gemm_unfused(shards, B, comm_block_rows, C=None, a_out=None, stream=None):

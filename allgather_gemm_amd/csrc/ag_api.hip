@@ -427,6 +427,92 @@ extern "C" int tgather(const void* const* shards, int32_t N, void* dst, int64_t 
                       elem_size, 0, stream);
 }
 
+extern "C" int gemm_rs(const void* A, const void* B, int32_t N, int32_t local_rank, int64_t M, int64_t Nc,
+                       int64_t K, const void* const* recv, void* P, void* out, int32_t mode, void* stream)
+{
+    if (N < 1 || N > kMaxShards || local_rank < 0 || local_rank >= N || M < 0 || Nc < 0 || K < 0)
+        return AG_EINVAL;
+    if (M % N != 0 || K % 8 != 0 || Nc % 8 != 0 || (mode != AG_RS_FUSED && mode != AG_RS_UNFUSED))
+        return AG_EINVAL;
+    if (K > (int64_t(1) << 21) || Nc * 32 * 2 > (int64_t(1) << 32))
+        return AG_EUNSUPPORTED;
+    if (M == 0 || Nc == 0)
+        return AG_OK;
+    const int64_t H = M / N;
+    if (!recv || !P || !out || !aligned16(P) || !aligned16(out))
+        return AG_EINVAL;
+    if (K > 0 && (!A || !B || !aligned16(A) || !aligned16(B)))
+        return AG_EINVAL;
+    for (int j = 0; j < N; ++j)
+        if (j != local_rank && (!recv[j] || !aligned16(recv[j])))
+            return AG_EINVAL;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    std::lock_guard<std::mutex> lock(g_mu);
+    Workspace* w = nullptr;
+    int rc;
+    if ((rc = current_ws(&w)) != AG_OK)
+        return rc;
+    const int64_t bm = gemm_tile_m();
+    const int64_t lo = (int64_t)local_rank * H, hi = lo + H;
+    const int64_t nrows = H > 0 ? (hi - 1) / bm - lo / bm + 1 : 0;   // GEMM tile rows meeting the block
+    if ((rc = ensure_flags(*w, nrows)) != AG_OK)
+        return rc;
+    if ((rc = begin_use(*w, s)) != AG_OK)
+        return rc;
+    if ((rc = next_epoch(*w, s)) != AG_OK)
+        return rc;
+
+    GemmArgs g;
+    std::memset(&g, 0, sizeof g);
+    g.A = A;
+    g.B = B;
+    g.C = P;
+    g.M = M;
+    g.Nc = Nc;
+    g.K = K;
+    g.nshards = 1;
+    g.H = M;
+    g.cb = M > 0 ? M : 1;
+    g.status = w->ctl + 4;
+    g.out_scale = 1.0f;
+
+    RsArgs r;
+    std::memset(&r, 0, sizeof r);
+    for (int j = 0; j < N; ++j)
+        r.parts[j] = j == local_rank ? static_cast<const void*>(static_cast<const char*>(P) + lo * Nc * 2) : recv[j];
+    r.out = out;
+    r.nparts = N;
+    r.H = H;
+    r.Nc = Nc;
+    r.lo = lo;
+    r.bm = bm;
+    r.target = (uint32_t)((Nc + gemm_tile_n() - 1) / gemm_tile_n());
+    r.status = w->ctl + 4;
+    r.epoch = w->epoch;
+    r.spin_limit = (int64_t)10000000 * 100;   // 10 s of the 100 MHz clock
+
+    if (mode == AG_RS_UNFUSED || H == 0) {
+        AG_HIP(launch_gemm(g, kGemmPlain, nullptr, s), "launch gemm");
+        AG_HIP(launch_rs_reduce(r, 4, s), "launch reduce");
+        return end_use(*w, s);
+    }
+    // fused: tile-row counts start at zero; the reduction waits on them from a second stream.  They
+    // live in the piece-count array, which every call that uses it zeroes first (the progress
+    // flags hold epochs and must never hold a count).
+    g.tile_done = w->done;
+    g.pub_lo = lo;
+    g.pub_hi = hi;
+    r.tile_done = w->done;
+    AG_HIP(launch_fill_u32(w->done, nrows, 0u, s), "clear tile counts");
+    AG_HIP(hipEventRecord(w->fork, s), "hipEventRecord(fork)");
+    AG_HIP(hipStreamWaitEvent(w->side, w->fork, 0), "hipStreamWaitEvent(side)");
+    AG_HIP(launch_rs_reduce(r, 1, w->side), "launch reduce");
+    AG_HIP(launch_gemm(g, kGemmPlain, nullptr, s), "launch gemm");
+    AG_HIP(hipEventRecord(w->join, w->side), "hipEventRecord(join)");
+    AG_HIP(hipStreamWaitEvent(s, w->join, 0), "hipStreamWaitEvent(join)");
+    return end_use(*w, s);
+}
+
 extern "C" int ag_gemm_noalloc(const void* const* shards, int32_t N, int64_t M, int64_t K, const void* B,
                                int64_t Nc, void* C, int64_t comm_block_rows, void* a_out, int32_t local_rank,
                                void* stream)

@@ -659,6 +659,12 @@ __device__ __forceinline__ void gemm_body(KParams p)
         // FP8 output (the FP8_OUTPUT variant of [AGMM] MatMul 按需等待): the 8 values, times
         // out_scale, go through the hardware's E4M3 "fn" conversion (round to nearest even, NaN
         // beyond 448: the conversion of torch.float8_e4m3fn) and leave as 8 bytes.
+        // GEMM + ReduceScatter: this tile holds rows another kernel reduces as soon as their tile row
+        // is complete, so its C goes out write-through (in memory once this wave's store count
+        // drains, dirty in no L2), and the tile is counted after every wave's stores have drained.
+        // Only with Nc % 8 == 0 (the caller checks).
+        const bool publish = MODE == kGemmPlain && a.tile_done != nullptr && tc.m0 < a.pub_hi &&
+                             tc.m0 + BM > a.pub_lo;
         {
             char* slab = (wave < 2 ? sA0 : sB0) + (wave & 1) * 16384;
             const int64_t wrow0 = tc.m0 + wm * 128, wcol0 = tc.n0 + wn * 128;
@@ -715,7 +721,12 @@ __device__ __forceinline__ void gemm_body(KParams p)
                     o[5] = (__bf16)x1[1];
                     o[6] = (__bf16)x1[2];
                     o[7] = (__bf16)x1[3];
-                    if (grow < a.M) {
+                    if (publish) {
+                        const __amdgpu_buffer_rsrc_t rc =
+                            make_rsrc(C + (wrow0 + i * 32) * a.Nc + wcol0, (uint32_t)(32 * a.Nc * 2));
+                        if (grow < a.M && gcol + 8 <= a.Nc)
+                            store_wt(rc, (uint32_t)((r * a.Nc + c8) * 2), __builtin_bit_cast(i32x4, o));
+                    } else if (grow < a.M) {
                         __bf16* dstp = C + grow * a.Nc + gcol;
                         if (vec_ok && gcol + 8 <= a.Nc) {
                             *reinterpret_cast<bf16x8*>(dstp) = o;
@@ -739,7 +750,11 @@ __device__ __forceinline__ void gemm_body(KParams p)
             }
             barrier_after_lds_write();   // s_ready is visible; LDS is free for the next tile's loads
         } else {
+            if (publish)
+                wait_vmcnt0();
             __syncthreads();   // LDS is free again for the next tile's loads
+            if (publish && wave0)
+                (void)wave_fetch_add(&a.tile_done[tc.m0 / BM - a.pub_lo / BM], 1u);
         }
     }
     if (MODE == kGemmFused) {
@@ -825,6 +840,8 @@ KParams make_params(const GemmArgs& a, GemmMode mode)
         p.pm = pm_make(a.H, a.cb, a.nshards, a.local_rank, a.K, BM, PIECE_BYTES);
         p.npieces = a.copy_pieces ? p.pm.nchunks * p.pm.ppc : 0;
         p.trickle = a.copy_pieces == 1 ? 1 : 0;
+    } else if (a.tile_done) {
+        p.pivot = (int)((a.pub_lo / BM) % p.num_pid_m);   // the reducing rank's rows first
     }
     return p;
 }

@@ -54,7 +54,33 @@ struct GemmArgs {
     int64_t spin_limit;     // 100 MHz ticks of one flag wait before giving up
     int out_fp8;            // C is FP8 E4M3 "fn" bytes (else bf16)
     float out_scale;        // FP8 output: C = e4m3fn(acc * out_scale)
+    // GEMM + ReduceScatter (plain mode): tiles holding rows [pub_lo, pub_hi) of C store them
+    // write-through and then count themselves in tile_done[tile row - pub_lo / BM]; the tile walk
+    // starts at pub_lo.  nullptr: no publishing.
+    uint32_t* tile_done;
+    int64_t pub_lo, pub_hi;
 };
+
+// --------------------------------------------------------------------- GEMM + ReduceScatter
+// One rank's block of the ReduceScatter: out = sum over j of parts[j], (H, Nc) bf16 each, summed in
+// fp32 in ascending j and rounded to bf16.  With tile_done, block row i waits until its tile row of
+// the GEMM (row lo + i of P) has `target` finished tiles.
+struct RsArgs {
+    const void* parts[kMaxShards];
+    void* out;
+    int nparts;
+    int64_t H, Nc;
+    int64_t lo;             // first row of the block in the GEMM's C
+    int64_t bm;             // GEMM tile rows
+    uint32_t* tile_done;    // nullptr: no waits (the serial schedule)
+    uint32_t target;        // tiles per tile row
+    uint32_t* status;       // [code, chunk, tile, epoch of the failing call]
+    uint32_t epoch;
+    int64_t spin_limit;     // 100 MHz ticks of one wait
+};
+
+// wgs_per_cu: 1 beside the GEMM (room for one wave per SIMD), more when it runs alone
+hipError_t launch_rs_reduce(const RsArgs& r, int wgs_per_cu, hipStream_t stream);
 
 // Piece plan of one fused call.
 struct FusedPlan {

@@ -137,6 +137,32 @@ int tgather_ex(const void *const *shards, int32_t N, void *dst, int64_t D0, int6
                int64_t D2, int64_t H, int64_t W, int64_t dst_rows, int64_t valid_rows,
                int64_t valid_cols, int32_t elem_size, int32_t root, void *stream);
 
+/*
+ * GEMM + ReduceScatter, one rank's share ([AGMM] 从集合通信理解数据流: ReduceScatter leaves rank r
+ * with the reduction, over all ranks, of block r; the mirror of the AllGather feeding the MatMul).
+ * In the row-parallel form every rank multiplies its K slice, P = A * B^T, and the ranks reduce P
+ * over row blocks of H = M / N rows.  On one GPU the other ranks' partials for this rank's rows
+ * arrive as input buffers.
+ *   A                 (M, K) bf16: this rank's K slice of the activations
+ *   B                 (Nc, K) bf16: this rank's K slice of the weight
+ *   recv              host array of N device pointers; recv[j], j != local_rank, is rank j's
+ *                     (H, Nc) bf16 partial for rows [local_rank*H, (local_rank+1)*H);
+ *                     recv[local_rank] is ignored (may be NULL)
+ *   P                 (M, Nc) bf16 output: this rank's partial product, bf16 (nearest even) of the
+ *                     fp32 sums -- every row block, the others being what the peers would receive
+ *   out               (H, Nc) bf16 output: bf16 (nearest even) of the fp32 sum over j = 0..N-1, in
+ *                     that order, of the partials (this rank's own rows of P in slot local_rank)
+ *   mode              AG_RS_FUSED: a reducing kernel on a second stream starts on each GEMM tile
+ *                     row of the block as soon as that row's tiles are written; AG_RS_UNFUSED: the
+ *                     GEMM, then the reduction.  Both give bitwise the same P and out.
+ * M % N == 0, K % 8 == 0, Nc % 8 == 0; 16-byte aligned pointers.  A wait that gave up (10 s) is
+ * reported by ag_check.
+ */
+#define AG_RS_FUSED    0
+#define AG_RS_UNFUSED  1
+int gemm_rs(const void *A, const void *B, int32_t N, int32_t local_rank, int64_t M, int64_t Nc,
+            int64_t K, const void *const *recv, void *P, void *out, int32_t mode, void *stream);
+
 /* For callers that cannot allocate device memory: code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc.  The same product as ag_gemm (C, and the gathered A in
  * a_out), by the fused schedule with the in-kernel producer on `stream` alone.  It allocates

@@ -74,6 +74,22 @@ def test_ag_gemm_ex_rejects_bad_options():
                             ctypes.byref(opt)) == ag.AG_EINVAL
 
 
+def test_gemm_rs_rejects_bad_arguments():
+    L = ag.lib()
+    recv = ctypes.cast(_fake_ptrs(4), _vp)
+    ok = dict(A=_vp(0x20000), B=_vp(0x30000), N=4, local=1, M=64, Nc=64, K=32, recv=recv,
+              P=_vp(0x40000), out=_vp(0x50000), mode=0)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return L.gemm_rs(a["A"], a["B"], a["N"], a["local"], a["M"], a["Nc"], a["K"], a["recv"], a["P"],
+                         a["out"], a["mode"], None)
+    for kw in (dict(N=0), dict(local=4), dict(local=-1), dict(M=66), dict(K=30), dict(Nc=60), dict(mode=2),
+               dict(P=_vp(0x40004)), dict(out=None), dict(A=None), dict(recv=None)):
+        assert call(**kw) == ag.AG_EINVAL, kw
+    assert call(M=0) == ag.AG_OK and call(Nc=0) == ag.AG_OK
+
+
 def test_empty_shapes_enqueue_nothing():
     L = ag.lib()
     ptrs = ctypes.cast(_fake_ptrs(2), _vp)

@@ -1,5 +1,6 @@
 """The fused GEMM kernels run next to the side-stream copy kernel (and, with the copy-engine producer,
-next to the runtime's small flag-writing kernels) on every CU, one wave of each per SIMD.  That only
+next to the runtime's small flag-writing kernels) on every CU, one wave of each per SIMD; in GEMM +
+ReduceScatter the plain GEMM kernel runs next to the reducing kernel the same way.  That only
 works if their VGPRs fit in one SIMD's 512 per lane together; if they do not, the copy cannot start
 while the GEMM waits for it, and every wait runs into its time-out.  This compiles the kernel source
 for gfx950 (no GPU needed) and checks the budget from the compiler's own kernel metadata."""
@@ -10,17 +11,17 @@ import subprocess
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-SRC = os.path.join(ROOT, "allgather_gemm_amd", "csrc", "ag_gemm.hip")
+CSRC = os.path.join(ROOT, "allgather_gemm_amd", "csrc")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 GRANULE = 8          # VGPR allocation granule per wave (gfx950, wave64)
 VGPRS_PER_LANE = 512
 
 
-def kernel_vgprs(tmp_path):
-    out = tmp_path / "ag_gemm.s"
+def kernel_vgprs(tmp_path, src):
+    out = tmp_path / (src + ".s")
     cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
-           "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "--cuda-device-only", "-S", SRC,
-           "-o", str(out)]
+           "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "--cuda-device-only", "-S",
+           os.path.join(CSRC, src), "-o", str(out)]
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-2000:]
     text = out.read_text()
@@ -37,9 +38,20 @@ def alloc(v):
 
 @pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
 def test_fused_gemm_and_concurrent_copy_kernel_fit_on_one_simd(tmp_path):
-    vg = kernel_vgprs(tmp_path)
+    vg = kernel_vgprs(tmp_path, "ag_gemm.hip")
     fused = {n: v for n, v in vg.items() if "gemm_fused" in n}
     copy = [v for n, v in vg.items() if "producer_kernelILi8E" in n]
     assert len(fused) == 2 and len(copy) == 1, sorted(vg)
     for name, v in fused.items():
         assert alloc(v) + alloc(copy[0]) <= VGPRS_PER_LANE, (name, v, copy[0])
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
+def test_plain_gemm_and_reducing_kernel_fit_on_one_simd(tmp_path):
+    vg = kernel_vgprs(tmp_path, "ag_gemm.hip")
+    rs = kernel_vgprs(tmp_path, "rs.hip")
+    plain = [v for n, v in vg.items() if "gemm_plain" in n]
+    red = [v for n, v in rs.items() if "rs_reduce" in n]
+    assert len(plain) == 1 and len(red) >= 1, (sorted(vg), sorted(rs))
+    for v in red:
+        assert alloc(plain[0]) + alloc(v) <= VGPRS_PER_LANE, (plain[0], v)

@@ -97,6 +97,46 @@ def make_ag_gemm_integers(N: int, H: int, K: int, Nc: int, seed: int = 0, lim: i
     return shards, B
 
 
+@dataclass(frozen=True)
+class GemmRsConfig:
+    """One rank's GEMM + ReduceScatter: A (M, K) and B (Nc, K) are the rank's K slices; the other
+    N - 1 ranks' partials for its rows are (M / N, Nc) each."""
+    name: str
+    N: int
+    M: int
+    K: int
+    Nc: int
+    local: int = 0
+    a_std: float = 1.0
+    b_std: float = 0.02
+    seed: int = 0
+
+    @property
+    def H(self) -> int:
+        return self.M // self.N
+
+    @property
+    def flops(self) -> int:
+        return 2 * self.M * self.Nc * self.K
+
+
+RS_TINY = GemmRsConfig("gemm_rs_tiny_4x512x64x256", N=4, M=512, K=64, Nc=256, local=1, b_std=1.0)
+# the square AG-GEMM workload's reduce-scatter mirror: K = 8192 split over 8 ranks
+RS_SQUARE = GemmRsConfig("gemm_rs_8192x8192x1024_n8", N=8, M=8192, K=1024, Nc=8192, local=0)
+
+
+def make_gemm_rs(cfg: GemmRsConfig, seed: int | None = None):
+    """(A (M,K), B (Nc,K), recv: N tensors (H, Nc), recv[local] None) bf16 CPU tensors.  The peers'
+    partials have the scale of a partial product, N(0, K a_std^2 b_std^2)."""
+    g = torch.Generator().manual_seed(cfg.seed if seed is None else seed)
+    A = (torch.randn(cfg.M, cfg.K, generator=g) * cfg.a_std).to(torch.bfloat16)
+    B = (torch.randn(cfg.Nc, cfg.K, generator=g) * cfg.b_std).to(torch.bfloat16)
+    sd = (cfg.K ** 0.5) * cfg.a_std * cfg.b_std
+    recv = [None if j == cfg.local else (torch.randn(cfg.H, cfg.Nc, generator=g) * sd).to(torch.bfloat16)
+            for j in range(cfg.N)]
+    return A, B, recv
+
+
 def make_tgather(N: int, D: tuple, H: int, W: int, dtype: torch.dtype, seed: int = 0,
                  bits: bool = False):
     """Returns a list of N contiguous CPU tensors of shape (D0, D1, D2, H, W)."""
