@@ -34,7 +34,8 @@ _i32, _i64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
 class AgOptions(ctypes.Structure):
     _fields_ = [("mode", _i32), ("local_rank", _i32), ("a_out", _vp), ("timeout_us", _i64),
                 ("reverse_order", _i32), ("skip_producer", _i32), ("producer", _i32),
-                ("gemm_events", _vp * 2), ("out_dtype", _i32), ("out_scale", ctypes.c_float)]
+                ("gemm_events", _vp * 2), ("out_dtype", _i32), ("out_scale", ctypes.c_float),
+                ("wait_stats", _vp)]
 
 
 class AgError(RuntimeError):
@@ -115,13 +116,15 @@ def ag_gemm(shards, B: torch.Tensor, comm_block_rows: int, C: torch.Tensor | Non
             mode: str = "fused", local_rank: int = 0, a_out: torch.Tensor | None = None,
             timeout_us: int = 0, reverse_order: bool = False, skip_producer: bool = False,
             producer: str = "side_stream", gemm_events=None, stream=None, out_dtype: str = "bf16",
-            out_scale: float = 1.0) -> torch.Tensor:
+            out_scale: float = 1.0, wait_stats: torch.Tensor | None = None) -> torch.Tensor:
     """C (M, Nc) = concat(shards) @ B^T.  shards: N tensors (H, K) bf16; B: (Nc, K) bf16.
 
     mode: "fused" | "unfused" | "gemm_only" | "plain_gemm"; producer (fused only): "side_stream" |
     "in_kernel" | "copy_engine".  out_dtype: "bf16" or "fp8_e4m3" (C = e4m3fn(sum * out_scale), a
     torch.float8_e4m3fn tensor).  gemm_events: optional (start, end) torch.cuda.Event pair that the
-    library records around the GEMM kernel's launch.  The call is asynchronous on `stream`; check()
+    library records around the GEMM kernel's launch.  wait_stats: optional int64 device tensor of 4
+    counters the GEMM adds to (flag-wait ticks at 100 MHz summed over workgroups, waits, pieces
+    copied while waiting, tiles that skipped their wait).  The call is asynchronous on `stream`; check()
     reports a wait that gave up."""
     shards = list(shards)
     N = len(shards)
@@ -146,7 +149,12 @@ def ag_gemm(shards, B: torch.Tensor, comm_block_rows: int, C: torch.Tensor | Non
     ev = (_vp * 2)(*(int(e.event_id) for e in gemm_events)) if gemm_events else (_vp * 2)(None, None)
     opt = AgOptions(_MODES[mode], local_rank, a_out.data_ptr() if a_out is not None else None,
                     timeout_us, int(reverse_order), int(skip_producer), _PRODUCERS[producer], ev,
-                    out_code, float(out_scale))
+                    out_code, float(out_scale), None)
+    if wait_stats is not None:
+        _check_dev(wait_stats, "wait_stats")
+        if wait_stats.dtype != torch.int64 or wait_stats.numel() < 4:
+            raise ValueError("wait_stats must be an int64 device tensor of 4 counters")
+        opt.wait_stats = wait_stats.data_ptr()
     if a_out is not None:
         _check_dev(a_out, "a_out")
         if a_out.dtype != torch.bfloat16 or tuple(a_out.shape) != (M, K):

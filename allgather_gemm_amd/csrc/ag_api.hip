@@ -273,6 +273,7 @@ extern "C" int ag_gemm_ex(const void* const* shards, int32_t N, int64_t M, int64
     const int64_t timeout_us = (opt && opt->timeout_us > 0) ? opt->timeout_us : 10000000;
     g.spin_limit = timeout_us * 100;   // s_memrealtime runs at 100 MHz
     g.reverse_order = opt ? opt->reverse_order : 0;
+    g.wait_stats = opt ? static_cast<uint64_t*>(opt->wait_stats) : nullptr;
     g.out_fp8 = (opt && opt->out_dtype == AG_OUT_FP8_E4M3) ? 1 : 0;
     g.out_scale = (opt && opt->out_scale != 0.0f) ? opt->out_scale : 1.0f;
 

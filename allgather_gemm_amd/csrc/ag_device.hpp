@@ -107,6 +107,12 @@ __device__ __forceinline__ void wave_exchange(uint32_t* p, uint32_t v)
         (void)__hip_atomic_exchange(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+__device__ __forceinline__ void wave_add_u64(uint64_t* p, uint64_t v)
+{
+    if (is_lane0())
+        (void)__hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ uint32_t flag_peek(uint32_t* f) { return wave_fetch_add(f, 0u); }
 
 __device__ __forceinline__ void flag_publish(uint32_t* f, uint32_t value) { wave_exchange(f, value); }

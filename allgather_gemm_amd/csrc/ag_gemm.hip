@@ -223,11 +223,22 @@ __device__ int64_t decide_wait(const KParams& p, int64_t c, uint64_t t_start, in
 // wave-0 step that publishes and decides the next command.  Every branch is wave-uniform.  Once
 // this workgroup has given up, `failed` stays set and later waits return at once, so a failed
 // call ends within one timeout.
+// The workgroup's flag-wait counters (measurement aid): kept in LDS by wave 0 -- in registers they
+// would stay live across the K loop -- and added to the caller's counters once, when the workgroup
+// ends.  Every lane of wave 0 stores the same value (no lane condition): a lane-divergent branch at
+// the end of the tile's wait region keeps the compiler from proving the K loop's buffer resources
+// uniform, and it then wraps every tile load in a loop over the lanes.
+struct WaitStats {
+    uint64_t ticks, waits, copied, skipped;
+};
+
 __device__ void wait_rows(const KParams& p, int64_t m0, int64_t m1, int64_t tile, int tid, bool wave0,
-                          int64_t* s_cmd, bool& exhausted, bool& failed)
+                          int64_t* s_cmd, bool& exhausted, bool& failed, WaitStats* ws)
 {
     int64_t c_first, c_last;
     pm_chunks_of_rows(p.pm, m0, m1, c_first, c_last);
+    const uint64_t t_wait = __builtin_amdgcn_s_memrealtime();
+    uint64_t copied = 0;
     for (int64_t c = c_first; c <= c_last; ++c) {
         if (failed)
             break;
@@ -248,10 +259,12 @@ __device__ void wait_rows(const KParams& p, int64_t m0, int64_t m1, int64_t tile
                 failed = true;
                 break;
             }
-            if (cmd >= 0)
+            if (cmd >= 0) {
                 copy_pieces(p, cmd, cnt, tid);
-            else
+                copied += (uint64_t)cnt;
+            } else {
                 __builtin_amdgcn_s_sleep(4);
+            }
             if (wave0) {
                 if (cmd >= 0)
                     publish_range(p, cmd, cnt);
@@ -267,6 +280,11 @@ __device__ void wait_rows(const KParams& p, int64_t m0, int64_t m1, int64_t tile
     if (p.pm.row_bytes % 128 != 0)
         acquire_agent();
     __syncthreads();
+    if (wave0) {
+        ws->ticks += __builtin_amdgcn_s_memrealtime() - t_wait;
+        ws->waits += 1;
+        ws->copied += copied;
+    }
 }
 
 // Wave 0: the flags of the chunks under gathered rows [m0, m1), one per lane (lane i: the i-th
@@ -430,6 +448,7 @@ __device__ __forceinline__ void gemm_body(KParams p)
     __shared__ __attribute__((aligned(1024))) char sB1[TILE_BYTES];
     __shared__ int64_t s_cmd[2];
     __shared__ int32_t s_ready;    // wave 0's verdict on the next tile's chunks (all flags raised)
+    __shared__ WaitStats s_ws;
 
     const GemmArgs& a = p.a;
     const int tid = threadIdx.x;
@@ -476,6 +495,8 @@ __device__ __forceinline__ void gemm_body(KParams p)
     // trips) altogether.  Any other outcome takes the ordinary wait.
     uint32_t peek = 0;
     int peek_n = -1;
+    if (MODE == kGemmFused && wave0)
+        s_ws = WaitStats{0, 0, 0, 0};
 
     for (int64_t t = vid; t < num_tiles; t += G) {
         const TileCoord tc = tile_of(t, p.num_pid_m, p.num_pid_n, p.pivot);
@@ -490,9 +511,12 @@ __device__ __forceinline__ void gemm_body(KParams p)
                 const bool ready = t != vid && __builtin_amdgcn_readfirstlane(s_ready) != 0;
                 if (!ready) {
                     trickle_flush(kparams(), tr, lane);  // a piece this wave holds never waits on anything
-                    wait_rows(kparams(), tc.m0, m1, t, tid, wave0, s_cmd, exhausted, failed);
-                } else if (kparams().pm.row_bytes % 128 != 0) {
-                    acquire_agent();     // as at the end of an ordinary wait
+                    wait_rows(kparams(), tc.m0, m1, t, tid, wave0, s_cmd, exhausted, failed, &s_ws);
+                } else {
+                    if (kparams().pm.row_bytes % 128 != 0)
+                        acquire_agent();     // as at the end of an ordinary wait
+                    if (wave0)
+                        s_ws.skipped += 1;
                 }
             }
             a_base = static_cast<const char*>(a.A) + tc.m0 * K * 2;
@@ -756,6 +780,14 @@ __device__ __forceinline__ void gemm_body(KParams p)
             if (publish && wave0)
                 (void)wave_fetch_add(&a.tile_done[tc.m0 / BM - a.pub_lo / BM], 1u);
         }
+    }
+    if (MODE == kGemmFused && wave0 && kparams().a.wait_stats) {
+        uint64_t* st = kparams().a.wait_stats;
+        const WaitStats w = s_ws;      // written by this wave only
+        wave_add_u64(&st[0], w.ticks);
+        wave_add_u64(&st[1], w.waits);
+        wave_add_u64(&st[2], w.copied);
+        wave_add_u64(&st[3], w.skipped);
     }
     if (MODE == kGemmFused) {
         // the gathered output needs every chunk, also those no tile waited for: before it exits,

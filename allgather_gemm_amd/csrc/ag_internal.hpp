@@ -59,6 +59,10 @@ struct GemmArgs {
     // starts at pub_lo.  nullptr: no publishing.
     uint32_t* tile_done;
     int64_t pub_lo, pub_hi;
+    // measurement aid (fused schedule): nullptr, or 4 counters the GEMM adds to -- 100 MHz ticks its
+    // workgroups spent waiting on chunk flags, waits, pieces copied by waiting workgroups, tiles
+    // whose prefetched flags let them skip the wait
+    uint64_t* wait_stats;
 };
 
 // --------------------------------------------------------------------- GEMM + ReduceScatter

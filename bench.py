@@ -14,6 +14,8 @@ Besides the headline the JSON line carries, per the fused AllGather+MatMul artic
     GEMM-only (flags raised beforehand) and the plain GEMM alone -- as median / p10 / p90 of
     individually timed calls, cold (a 1 GiB write evicts L2 and the MALL before every call) and hot;
   * the MLP-up (16384 x 14336 x 4096) and ragged (4000 x 28672 x 8192) workloads the same way;
+  * GEMM + ReduceScatter (one rank's share of the square workload split over 8 ranks), fused and
+    serial;
   * TGATHER on its two workloads, cold and hot, as GB/s of algorithmic traffic;
   * the shader clock sampled while fused calls run back to back;
   * the CPU oracle timed on a bounded sample of the square workload.
@@ -204,6 +206,10 @@ def recorded_traffic(tag: str):
     return float(vals["hbm_bytes_per_launch"])
 
 
+def ag_cus(torch) -> int:
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
 def cpu_baseline(cfg, shards, B, target_s):
     """The oracle as it stands (naive ascending-k loop, gcc -O3, no -march, OpenMP) on a bounded
     sample: full rows of C, every column."""
@@ -304,6 +310,23 @@ def main():
     tflops = cfg.flops / (ms_fused * 1e-3) / 1e12
     kernel_tflops = cfg.flops / (gemm_kernel_ms * 1e-3) / 1e12
 
+    # how long the fused GEMM's tiles waited on chunk flags: 10 more calls, outside the timed steps
+    wst = torch.zeros(4, dtype=torch.int64, device=dev)
+    nw = 10
+    for _ in range(nw):
+        ag.ag_gemm(sd, Bd, cfg.cb, C=C, a_out=a_gath, wait_stats=wst)
+    torch.cuda.synchronize()
+    ticks, waits, copied, skipped = (int(v) for v in wst.cpu().tolist())
+    grid = min(ag_cus(torch), (cfg.M // 256) * (cfg.Nc // 256))
+    fused_waits = {
+        "calls": nw, "workgroups": grid,
+        "wait_us_per_call_summed_over_workgroups": round(ticks / 100.0 / nw, 2),
+        "wait_us_per_workgroup_per_call": round(ticks / 100.0 / nw / grid, 3),
+        "waits_per_call": waits / nw, "tiles_skipping_the_wait_per_call": skipped / nw,
+        "pieces_copied_by_waiting_tiles_per_call": copied / nw,
+        "pieces_per_call": cfg.N * ((cfg.H + cfg.cb - 1) // cfg.cb) * ((cfg.cb * cfg.K * 2 + 16383) // 16384),
+    }
+
     if args.headline_only:
         # one copy of known size, for scaling the memory counters of a profiled run: 256 MiB read
         # and written once each, with the caches evicted first so that every byte comes from HBM
@@ -314,6 +337,7 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"headline_only": True, "ms_per_step": round(ms_fused, 5),
                           "gemm_kernel_ms": round(gemm_kernel_ms, 5), "TFLOP/s": round(tflops, 2),
+                          "fused_waits": fused_waits,
                           "calibration_copy_bytes_each_way": 8 * 4096 * 4096 * 2}), flush=True)
         return
 
@@ -375,6 +399,31 @@ def main():
         del osd, oBd, oC, oa
         torch.cuda.empty_cache()
 
+    # GEMM + ReduceScatter, one rank's share, on the square workload split over 8 ranks
+    rcfg = workloads.RS_SQUARE
+    rA, rB, rrecv = workloads.make_gemm_rs(rcfg)
+    rAd, rBd = rA.to(dev), rB.to(dev)
+    rrd = [None if t is None else t.to(dev) for t in rrecv]
+    rP = torch.empty((rcfg.M, rcfg.Nc), dtype=torch.bfloat16, device=dev)
+    rout = torch.empty((rcfg.H, rcfg.Nc), dtype=torch.bfloat16, device=dev)
+    rs = {}
+    for name, fused in (("fused", True), ("unfused", False)):
+        fn = lambda k, fused=fused: ag.gemm_rs(rAd, rBd, rrd, rcfg.local, P=rP, out=rout, fused=fused)
+        cold, _ = time_each(torch, fn, reps, warm, stream, scrub=scrub)
+        hot, _ = time_each(torch, fn, reps, warm, stream)
+        rs[name] = {"cold": stats(cold), "hot": stats(hot)}
+        rs[name]["cold_tflops"] = round(rcfg.flops / (rs[name]["cold"]["median_ms"] * 1e-3) / 1e12, 2)
+    rc, info = ag.check()
+    if rc != ag.AG_OK:
+        print("gemm_rs reported %s %s" % (ag.status_str(rc), info), file=sys.stderr)
+        sys.exit(1)
+    rs["fused_vs_unfused_speedup_cold"] = round(rs["unfused"]["cold"]["median_ms"] / rs["fused"]["cold"]["median_ms"], 4)
+    rs["fused_vs_unfused_speedup_hot"] = round(rs["unfused"]["hot"]["median_ms"] / rs["fused"]["hot"]["median_ms"], 4)
+    rs["config"] = {"workload": rcfg.name, "M": rcfg.M, "K_per_rank": rcfg.K, "Nc": rcfg.Nc, "ranks": rcfg.N,
+                    "local_rank": rcfg.local}
+    del rAd, rBd, rrd, rP, rout
+    torch.cuda.empty_cache()
+
     # standalone TGATHER on its two workloads
     gathers = {}
     for tg in (workloads.TG_FP16, workloads.TG_RAGGED):
@@ -419,9 +468,11 @@ def main():
         "config": {"workload": cfg.name + " fused", "M": cfg.M, "K": cfg.K, "Nc": cfg.Nc,
                    "shards": cfg.N, "comm_block_rows": cfg.cb, "local_rank": 0, "producer": "side_stream"},
         "roofline": roofline,
+        "fused_waits": fused_waits,
         "schedules": sched,
         "workloads": other,
         "tgather": gathers,
+        "gemm_reduce_scatter": rs,
         "sclk": sclk,
         "protocol": {"reps": reps, "warmup_per_statistic": warm,
                      "cold": "1 GiB written before every timed call", "statistic": "median, p10, p90"},

@@ -82,6 +82,10 @@ typedef struct ag_options {
     int32_t out_dtype;     /* AG_OUT_*; with AG_OUT_FP8_E4M3, C is an (M, Nc) byte array */
     float out_scale;       /* AG_OUT_FP8_E4M3: factor applied to the fp32 sums before the
                               conversion; 0 means 1 (must be finite) */
+    void *wait_stats;      /* measurement aid (AG_MODE_FUSED): NULL, or a device array of 4 uint64 the
+                              GEMM adds to: 100 MHz clock ticks its workgroups spent waiting on chunk
+                              flags (summed over workgroups), waits, pieces copied by waiting
+                              workgroups, tiles that skipped their wait (flags read in advance) */
 } ag_options;
 
 /*

@@ -270,3 +270,28 @@ def test_full_size_workloads_every_element(cfg):
         assert torch.equal(a_out.view(torch.int16), A_d.view(torch.int16)), producer
         assert torch.equal(C_f.view(torch.int16), C_p.view(torch.int16)), producer
     assert ag.check()[0] == ag.AG_OK
+
+
+def test_wait_statistics_account_for_every_waiting_tile():
+    """The fused GEMM's wait counters (a measurement aid): every non-local tile either waits or
+    skips its wait, nothing is copied when every flag is already raised, and in-kernel copying shows
+    up as pieces copied by waiting tiles."""
+    N, H, K, Nc, cb = 4, 256, 256, 512, 64
+    print("wait statistics", flush=True)
+    A, shards, B = workloads.make_ag_gemm_shapes(N, H, K, Nc, seed=17)
+    sd, Bd = to_dev(A, shards, B)
+    a_out = A.to(DEV)
+    tiles_nonlocal = (N - 1) * (H // 256) * (Nc // 256)       # local shard 0: one tile row of 4
+    st = torch.zeros(4, dtype=torch.int64, device=DEV)
+    ag.ag_gemm(sd, Bd, cb, a_out=a_out, mode="gemm_only", wait_stats=st)
+    torch.cuda.synchronize()
+    ticks, waits, copied, skipped = st.cpu().tolist()
+    assert waits + skipped == tiles_nonlocal and copied == 0 and ticks >= 0
+    st.zero_()
+    a2 = torch.empty_like(a_out)
+    ag.ag_gemm(sd, Bd, cb, a_out=a2, producer="in_kernel", wait_stats=st)
+    torch.cuda.synchronize()
+    ticks, waits, copied, skipped = st.cpu().tolist()
+    assert waits + skipped == tiles_nonlocal and waits >= 1 and ticks > 0
+    assert torch.equal(a2.view(torch.int16), a_out.view(torch.int16))
+    assert ag.check()[0] == ag.AG_OK

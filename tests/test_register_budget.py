@@ -55,3 +55,25 @@ def test_plain_gemm_and_reducing_kernel_fit_on_one_simd(tmp_path):
     assert len(plain) == 1 and len(red) >= 1, (sorted(vg), sorted(rs))
     for v in red:
         assert alloc(plain[0]) + alloc(v) <= VGPRS_PER_LANE, (plain[0], v)
+
+
+@pytest.mark.skipif(not os.path.exists(HIPCC), reason="hipcc not installed")
+def test_gemm_tile_loads_use_a_uniform_buffer_resource(tmp_path):
+    """The K loop's global->LDS loads take their buffer resource from scalar registers.  If the
+    compiler cannot prove the resource uniform (a lane-0-only branch in the tile loop was enough to
+    break its analysis once), it wraps every load in a loop over the distinct values of the lanes
+    -- readfirstlane, compare, exec mask -- which cost the GEMM 8 %.  No such loop may appear."""
+    out = tmp_path / "ag_gemm.s"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-O3", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", "-I", os.path.join(ROOT, "include"), "--cuda-device-only", "-S",
+           os.path.join(CSRC, "ag_gemm.hip"), "-o", str(out)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    lines = out.read_text().splitlines()
+    n_dma = 0
+    for i, line in enumerate(lines):
+        if "offen lds" in line:
+            n_dma += 1
+            window = lines[max(0, i - 8):i]
+            assert not any("v_readfirstlane" in w for w in window), "\n".join(lines[max(0, i - 8):i + 1])
+    assert n_dma > 0
