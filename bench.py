@@ -23,6 +23,7 @@ Besides the headline the JSON line carries, per the fused AllGather+MatMul artic
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--reps R] [--no-cpu-baseline]
        python bench.py --headline-only ...   (headline steps only, for kernel traces and counters)
        python bench.py --tgather-only ...    (TGATHER workloads only, likewise)
+       python bench.py --rs-only ...         (GEMM + ReduceScatter only, likewise)
 """
 from __future__ import annotations
 
@@ -61,6 +62,8 @@ def parse():
                     help="only the headline steps (plus one calibration copy): for rocprofv3 runs")
     ap.add_argument("--tgather-only", action="store_true",
                     help="only TGATHER on its two workloads, --steps calls each: for rocprofv3 runs")
+    ap.add_argument("--rs-only", action="store_true",
+                    help="only GEMM + ReduceScatter, --steps fused then --steps serial calls: for rocprofv3 runs")
     return ap.parse_args()
 
 
@@ -251,6 +254,28 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
+
+    if args.rs_only:
+        rcfg = workloads.RS_SQUARE
+        rA, rB, rrecv = workloads.make_gemm_rs(rcfg)
+        rAd, rBd = rA.to(dev), rB.to(dev)
+        rrd = [None if t is None else t.to(dev) for t in rrecv]
+        rP = torch.empty((rcfg.M, rcfg.Nc), dtype=torch.bfloat16, device=dev)
+        rout = torch.empty((rcfg.H, rcfg.Nc), dtype=torch.bfloat16, device=dev)
+        out = {}
+        for name, fused in (("fused", True), ("unfused", False)):
+            for _ in range(args.warmup):
+                ag.gemm_rs(rAd, rBd, rrd, rcfg.local, P=rP, out=rout, fused=fused)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(args.steps):
+                ag.gemm_rs(rAd, rBd, rrd, rcfg.local, P=rP, out=rout, fused=fused)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            out[name + "_ms_per_call"] = round(e0.elapsed_time(e1) / args.steps, 5)
+        print(json.dumps({"rs_only": True, "workload": rcfg.name, **out}), flush=True)
+        return
 
     if args.tgather_only:
         out = {}
@@ -475,7 +500,7 @@ def main():
         "gemm_reduce_scatter": rs,
         "sclk": sclk,
         "protocol": {"reps": reps, "warmup_per_statistic": warm,
-                     "cold": "1 GiB written before every timed call", "statistic": "median, p10, p90"},
+                     "cold": "1 GiB read (torch amax) before every timed call", "statistic": "median, p10, p90"},
     }
     if cpu is not None:
         line["cpu_baseline"] = cpu
