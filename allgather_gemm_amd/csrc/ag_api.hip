@@ -325,17 +325,15 @@ extern "C" int ag_gemm_ex(const void* const* shards, int32_t N, int64_t M, int64
         if ((rc = gemm_timed(g, kGemmFused, &f, s, opt)) != AG_OK)
             return rc;
     } else if (producer == AG_PRODUCER_SIDE_STREAM) {
-        // the first wave's chunks are copied by the whole GPU before the GEMM starts; the rest by a
-        // copy kernel on the side stream while the GEMM runs (waiting tiles help); the call ends
-        // when both kernels have
+        // the first wave's chunks are copied by the whole GPU before the GEMM starts (the same
+        // kernel resets the call's counters); the rest by a copy kernel on the side stream while
+        // the GEMM runs (waiting tiles help); the call ends when both kernels have
         g.copy_pieces = kCopyWaiters;
         const FusedPlan f = plan_fused(g);
-        AG_HIP(launch_reset(g, f, s), "reset piece counters");
-        if (f.fill_end > 0)
-            AG_HIP(launch_producer(g, f, true, s), "launch fill copy");
+        AG_HIP(launch_fill(g, f, s), "launch fill copy");
         AG_HIP(hipEventRecord(w->fork, s), "hipEventRecord(fork)");
         AG_HIP(hipStreamWaitEvent(w->side, w->fork, 0), "hipStreamWaitEvent(side)");
-        AG_HIP(launch_producer(g, f, false, w->side), "launch producer");
+        AG_HIP(launch_producer(g, f, w->side), "launch producer");
         if ((rc = gemm_timed(g, kGemmFused, &f, s, opt)) != AG_OK)
             return rc;
         AG_HIP(hipEventRecord(w->join, w->side), "hipEventRecord(join)");

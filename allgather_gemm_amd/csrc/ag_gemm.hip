@@ -822,9 +822,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_fused_trickle_kernel(KParams p)
     gemm_body<kGemmFused, true>(p);
 }
 
-// Copy kernel of the side-stream schedule.  Beside the GEMM (U = 8) it is small -- no LDS tile, few
-// VGPRs -- so its workgroups fit next to the GEMM's; alone on the GPU, for the pipeline fill
-// (U = 16), it keeps more loads in flight per lane.
+// Copy kernel of the side-stream schedule, beside the GEMM.  It is small -- no LDS tile, few VGPRs --
+// so its workgroups fit next to the GEMM's.
 template <int U>
 __global__ __launch_bounds__(NT) void producer_kernel(KParams p, uint32_t* ctr, int64_t end)
 {
@@ -832,6 +831,58 @@ __global__ __launch_bounds__(NT) void producer_kernel(KParams p, uint32_t* ctr, 
     const int tid = threadIdx.x;
     const bool wave0 = __builtin_amdgcn_readfirstlane(tid >> 6) == 0;
     drain_pieces<U>(p, ctr, end, tid, wave0, s_cmd);
+}
+
+// Start of a side-stream fused call, alone on the GPU before the GEMM and the copy kernel beside it:
+// pieces [0, fill_end) -- every chunk the first wave of tiles reads -- are copied by the whole GPU,
+// FILL_PIECES pieces per workgroup in one pass (each lane's loads all in flight, then its stores;
+// units past a piece's end read zeros and store nothing, so no lane takes a branch); the flags of
+// those chunks are raised, the piece counters start past them and the per-chunk piece counts at
+// zero.  Nothing reads the flags, counters or copied rows before this kernel has ended.
+constexpr int FILL_PIECES = 4;
+constexpr int FILL_UNITS = (int)(PIECE_BYTES / 16 / NT);   // 16-byte units per lane per piece
+static_assert(FILL_UNITS * 16 * NT == PIECE_BYTES, "a piece is a whole number of 16-byte units per lane");
+
+__global__ __launch_bounds__(NT) void fill_kernel(KParams p)
+{
+    const GemmArgs& a = p.a;
+    const int tid = threadIdx.x;
+    const int64_t gid = (int64_t)blockIdx.x * NT + tid, gsize = (int64_t)gridDim.x * NT;
+    if (gid == 0) {
+        a.ticket[0] = (uint32_t)p.fill_end;   // a waiting tile finds the fill's pieces taken
+        a.ticket[1] = (uint32_t)p.fill_end;
+    }
+    for (int64_t i = gid; i < p.pm.nchunks; i += gsize)
+        a.done[i] = 0;
+    for (int64_t pos = gid; pos < p.fill_end / p.pm.ppc; pos += gsize)
+        a.flags[pm_ready_chunk(p.pm, pos)] = a.epoch;
+    const int64_t q0 = (int64_t)blockIdx.x * FILL_PIECES;
+    __amdgpu_buffer_rsrc_t src[FILL_PIECES], dst[FILL_PIECES];
+#pragma unroll
+    for (int j = 0; j < FILL_PIECES; ++j) {
+        int64_t bytes = 0;
+        const char* from = static_cast<const char*>(a.A);
+        const char* to = static_cast<const char*>(a.A);
+        if (q0 + j < p.fill_end) {
+            const PieceSpan sp = piece_at(p, q0 + j);
+            from = static_cast<const char*>(a.shards[sp.shard]) + sp.src_off;
+            to += sp.dst_off;
+            bytes = sp.bytes;
+        }
+        src[j] = span_rsrc(from, bytes);
+        dst[j] = span_rsrc(to, bytes);
+    }
+    i32x4 v[FILL_PIECES][FILL_UNITS];
+#pragma unroll
+    for (int j = 0; j < FILL_PIECES; ++j)
+#pragma unroll
+        for (int u = 0; u < FILL_UNITS; ++u)
+            v[j][u] = __builtin_amdgcn_raw_buffer_load_b128(src[j], (uint32_t)((tid + u * NT) * 16), 0, 0);
+#pragma unroll
+    for (int j = 0; j < FILL_PIECES; ++j)
+#pragma unroll
+        for (int u = 0; u < FILL_UNITS; ++u)
+            store_wt(dst[j], (uint32_t)((tid + u * NT) * 16), v[j][u]);
 }
 
 // Start of a fused call: piece counters, per-chunk piece counts.  A call that gave up leaves its
@@ -982,7 +1033,7 @@ hipError_t launch_gemm(const GemmArgs& a, GemmMode mode, const FusedPlan* f, hip
     return hipGetLastError();
 }
 
-hipError_t launch_producer(const GemmArgs& a, const FusedPlan& f, bool fill, hipStream_t stream)
+hipError_t launch_producer(const GemmArgs& a, const FusedPlan& f, hipStream_t stream)
 {
     int cus = 0;
     hipError_t e = num_cus(&cus);
@@ -990,16 +1041,22 @@ hipError_t launch_producer(const GemmArgs& a, const FusedPlan& f, bool fill, hip
         return e;
     KParams p = make_params(a, kGemmFused);
     p.fill_end = f.fill_end;
-    uint32_t* ctr = fill ? a.ticket : a.ticket + 1;
-    const int64_t first = fill ? 0 : f.fill_end, end = fill ? f.fill_end : p.npieces;
-    if (end <= first)
+    if (p.npieces <= f.fill_end)
         return hipSuccess;
-    const int64_t batches = (end - first + WAIT_BATCH - 1) / WAIT_BATCH;
+    const int64_t batches = (p.npieces - f.fill_end + WAIT_BATCH - 1) / WAIT_BATCH;
     const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(batches, cus));
-    if (fill)
-        producer_kernel<16><<<grid, NT, 0, stream>>>(p, ctr, end);
-    else
-        producer_kernel<8><<<grid, NT, 0, stream>>>(p, ctr, end);
+    producer_kernel<8><<<grid, NT, 0, stream>>>(p, a.ticket + 1, p.npieces);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill(const GemmArgs& a, const FusedPlan& f, hipStream_t stream)
+{
+    KParams p = make_params(a, kGemmFused);
+    p.fill_end = f.fill_end;
+    const int64_t grid = std::max<int64_t>(1, (f.fill_end + FILL_PIECES - 1) / FILL_PIECES);
+    if (grid > INT32_MAX)
+        return hipErrorInvalidValue;
+    fill_kernel<<<(int)grid, NT, 0, stream>>>(p);
     return hipGetLastError();
 }
 

@@ -100,9 +100,14 @@ hipError_t launch_reset(const GemmArgs& a, const FusedPlan& f, hipStream_t strea
 
 hipError_t launch_gemm(const GemmArgs& a, GemmMode mode, const FusedPlan* f, hipStream_t stream);
 
-// Copy kernel of the side-stream schedule: with fill, pieces [0, fill_end) (alone on the GPU,
-// before the GEMM); else the rest, beside the GEMM.  It never waits.
-hipError_t launch_producer(const GemmArgs& a, const FusedPlan& f, bool fill, hipStream_t stream);
+// Start of a side-stream fused call (in place of launch_reset): copies pieces [0, fill_end) with the
+// whole GPU, raises their chunks' flags, starts both piece counters at fill_end and zeroes the
+// per-chunk piece counts.
+hipError_t launch_fill(const GemmArgs& a, const FusedPlan& f, hipStream_t stream);
+
+// Copy kernel of the side-stream schedule: pieces [fill_end, npieces), beside the GEMM.  It never
+// waits.
+hipError_t launch_producer(const GemmArgs& a, const FusedPlan& f, hipStream_t stream);
 
 hipError_t device_cus(int* out);
 
