@@ -44,6 +44,8 @@ constexpr int SLOTS = BM * BK * 2 / 16;        // 16-byte slots per operand tile
 constexpr int TILE_BYTES = SLOTS * 16;         // 32 KiB per operand tile
 constexpr int GROUP_M = 8;                     // tile rows per group of the grouped order
 constexpr int64_t PIECE_BYTES = 16 * 1024;     // bytes per copy piece
+constexpr int PIECE_UNITS = (int)(PIECE_BYTES / 16 / NT);   // 16-byte units per lane per piece
+static_assert(PIECE_UNITS * 16 * NT == PIECE_BYTES, "a piece is a whole number of 16-byte units per lane");
 constexpr int WAIT_BATCH = 4;                  // pieces a waiting workgroup takes at a time
 constexpr int SLICE = 1024;                    // bytes a wave copies per K step in the background
 
@@ -157,8 +159,12 @@ __device__ __forceinline__ int64_t take(uint32_t* ctr, int64_t end, uint32_t wan
     return (int64_t)t;
 }
 
-// All threads of the workgroup: copy pieces [q0, q0 + n) with 16-byte loads/stores (U in flight per
-// lane), drain, barrier.  After it, one wave's release covers every byte.
+// Copies pieces [q0, q0 + n) with the whole workgroup, then drains its stores and meets at a barrier
+// (after it, one wave's release covers every byte).  A 16 KiB piece is four 16-byte units per lane,
+// fewer than the unrolled loop takes, so each lane copies them one load and store at a time: a
+// gentle copy.  Keeping every unit in flight copied faster, but no side-stream call got faster and
+// in-kernel calls got slower (their waiting and draining workgroups then pressed harder on the
+// memory system the running tiles use).
 template <int U = 8>
 __device__ void copy_pieces(const KParams& p, int64_t q0, int64_t n, int tid)
 {
@@ -840,8 +846,6 @@ __global__ __launch_bounds__(NT) void producer_kernel(KParams p, uint32_t* ctr, 
 // those chunks are raised, the piece counters start past them and the per-chunk piece counts at
 // zero.  Nothing reads the flags, counters or copied rows before this kernel has ended.
 constexpr int FILL_PIECES = 4;
-constexpr int FILL_UNITS = (int)(PIECE_BYTES / 16 / NT);   // 16-byte units per lane per piece
-static_assert(FILL_UNITS * 16 * NT == PIECE_BYTES, "a piece is a whole number of 16-byte units per lane");
 
 __global__ __launch_bounds__(NT) void fill_kernel(KParams p)
 {
@@ -869,19 +873,23 @@ __global__ __launch_bounds__(NT) void fill_kernel(KParams p)
             to += sp.dst_off;
             bytes = sp.bytes;
         }
-        src[j] = span_rsrc(from, bytes);
-        dst[j] = span_rsrc(to, bytes);
+        // the values are the same in every lane; saying so keeps the copies free of per-lane loops
+        // over the buffer resources
+        src[j] = span_rsrc(reinterpret_cast<const char*>(uniform_i64(reinterpret_cast<int64_t>(from))),
+                           uniform_i64(bytes));
+        dst[j] = span_rsrc(reinterpret_cast<const char*>(uniform_i64(reinterpret_cast<int64_t>(to))),
+                           uniform_i64(bytes));
     }
-    i32x4 v[FILL_PIECES][FILL_UNITS];
+    i32x4 v[FILL_PIECES][PIECE_UNITS];
 #pragma unroll
     for (int j = 0; j < FILL_PIECES; ++j)
 #pragma unroll
-        for (int u = 0; u < FILL_UNITS; ++u)
+        for (int u = 0; u < PIECE_UNITS; ++u)
             v[j][u] = __builtin_amdgcn_raw_buffer_load_b128(src[j], (uint32_t)((tid + u * NT) * 16), 0, 0);
 #pragma unroll
     for (int j = 0; j < FILL_PIECES; ++j)
 #pragma unroll
-        for (int u = 0; u < FILL_UNITS; ++u)
+        for (int u = 0; u < PIECE_UNITS; ++u)
             store_wt(dst[j], (uint32_t)((tid + u * NT) * 16), v[j][u]);
 }
 
