@@ -24,7 +24,9 @@ _MODES = {"fused": MODE_FUSED, "unfused": MODE_UNFUSED, "gemm_only": MODE_GEMM_O
           "plain_gemm": MODE_PLAIN_GEMM}
 PRODUCER_SIDE_STREAM, PRODUCER_IN_KERNEL, PRODUCER_COPY_ENGINE = 0, 1, 2
 OUT_BF16, OUT_FP8_E4M3 = 0, 1
+IN_BF16, IN_FP8_E4M3 = 0, 1
 _OUT = {"bf16": (OUT_BF16, torch.bfloat16), "fp8_e4m3": (OUT_FP8_E4M3, torch.float8_e4m3fn)}
+_IN = {"bf16": (IN_BF16, (torch.bfloat16,)), "fp8_e4m3": (IN_FP8_E4M3, (torch.float8_e4m3fn, torch.uint8))}
 _PRODUCERS = {"in_kernel": PRODUCER_IN_KERNEL, "side_stream": PRODUCER_SIDE_STREAM,
               "copy_engine": PRODUCER_COPY_ENGINE}
 
@@ -35,7 +37,7 @@ class AgOptions(ctypes.Structure):
     _fields_ = [("mode", _i32), ("local_rank", _i32), ("a_out", _vp), ("timeout_us", _i64),
                 ("reverse_order", _i32), ("skip_producer", _i32), ("producer", _i32),
                 ("gemm_events", _vp * 2), ("out_dtype", _i32), ("out_scale", ctypes.c_float),
-                ("wait_stats", _vp)]
+                ("wait_stats", _vp), ("in_dtype", _i32)]
 
 
 class AgError(RuntimeError):
@@ -116,8 +118,11 @@ def ag_gemm(shards, B: torch.Tensor, comm_block_rows: int, C: torch.Tensor | Non
             mode: str = "fused", local_rank: int = 0, a_out: torch.Tensor | None = None,
             timeout_us: int = 0, reverse_order: bool = False, skip_producer: bool = False,
             producer: str = "side_stream", gemm_events=None, stream=None, out_dtype: str = "bf16",
-            out_scale: float = 1.0, wait_stats: torch.Tensor | None = None) -> torch.Tensor:
-    """C (M, Nc) = concat(shards) @ B^T.  shards: N tensors (H, K) bf16; B: (Nc, K) bf16.
+            out_scale: float = 1.0, wait_stats: torch.Tensor | None = None,
+            in_dtype: str = "bf16") -> torch.Tensor:
+    """C (M, Nc) = concat(shards) @ B^T.  shards: N tensors (H, K); B: (Nc, K), both bf16, or with
+    in_dtype="fp8_e4m3" both FP8 E4M3 "fn" (torch.float8_e4m3fn or their uint8 codes; K % 16 == 0),
+    when C = out_scale * (A B^T) (out_scale folds the inputs' per-tensor scales).
 
     mode: "fused" | "unfused" | "gemm_only" | "plain_gemm"; producer (fused only): "side_stream" |
     "in_kernel" | "copy_engine".  out_dtype: "bf16" or "fp8_e4m3" (C = e4m3fn(sum * out_scale), a
@@ -133,13 +138,14 @@ def ag_gemm(shards, B: torch.Tensor, comm_block_rows: int, C: torch.Tensor | Non
     H, K = shards[0].shape
     M = N * H
     Nc = B.shape[0]
+    in_code, in_types = _IN[in_dtype]
     for i, s in enumerate(shards):
         _check_dev(s, "shard %d" % i)
-        if s.dtype != torch.bfloat16 or tuple(s.shape) != (H, K):
-            raise ValueError("shards must all be (H, K) bfloat16")
+        if s.dtype not in in_types or tuple(s.shape) != (H, K):
+            raise ValueError("shards must all be (H, K) %s" % in_dtype)
     _check_dev(B, "B")
-    if B.dtype != torch.bfloat16 or B.shape[1] != K:
-        raise ValueError("B must be (Nc, K) bfloat16")
+    if B.dtype not in in_types or B.shape[1] != K:
+        raise ValueError("B must be (Nc, K) %s" % in_dtype)
     out_code, out_torch = _OUT[out_dtype]
     if C is None:
         C = torch.empty((M, Nc), dtype=out_torch, device=B.device)
@@ -149,7 +155,7 @@ def ag_gemm(shards, B: torch.Tensor, comm_block_rows: int, C: torch.Tensor | Non
     ev = (_vp * 2)(*(int(e.event_id) for e in gemm_events)) if gemm_events else (_vp * 2)(None, None)
     opt = AgOptions(_MODES[mode], local_rank, a_out.data_ptr() if a_out is not None else None,
                     timeout_us, int(reverse_order), int(skip_producer), _PRODUCERS[producer], ev,
-                    out_code, float(out_scale), None)
+                    out_code, float(out_scale), None, in_code)
     if wait_stats is not None:
         _check_dev(wait_stats, "wait_stats")
         if wait_stats.dtype != torch.int64 or wait_stats.numel() < 4:
@@ -157,8 +163,8 @@ def ag_gemm(shards, B: torch.Tensor, comm_block_rows: int, C: torch.Tensor | Non
         opt.wait_stats = wait_stats.data_ptr()
     if a_out is not None:
         _check_dev(a_out, "a_out")
-        if a_out.dtype != torch.bfloat16 or tuple(a_out.shape) != (M, K):
-            raise ValueError("a_out must be (M, K) bfloat16")
+        if a_out.dtype not in in_types or tuple(a_out.shape) != (M, K):
+            raise ValueError("a_out must be (M, K) %s" % in_dtype)
     rc = lib().ag_gemm_ex(ctypes.cast(_ptrs(shards), _vp), N, M, K, B.data_ptr(), Nc,
                           C.data_ptr(), comm_block_rows, _stream_ptr(stream), ctypes.byref(opt))
     if rc != AG_OK:

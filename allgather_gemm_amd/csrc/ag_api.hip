@@ -152,6 +152,10 @@ int validate_gemm(const void* const* shards, int32_t N, int64_t M, int64_t K, co
             return AG_EINVAL;
         if (opt->out_dtype != AG_OUT_BF16 && opt->out_dtype != AG_OUT_FP8_E4M3)
             return AG_EINVAL;
+        if (opt->in_dtype != AG_IN_BF16 && opt->in_dtype != AG_IN_FP8_E4M3)
+            return AG_EINVAL;
+        if (opt->in_dtype == AG_IN_FP8_E4M3 && K % 16 != 0)
+            return AG_EINVAL;   // rows of whole 16-byte chunks
         if (!std::isfinite(opt->out_scale))
             return AG_EINVAL;
         if (opt->a_out && !aligned16(opt->a_out))
@@ -241,9 +245,11 @@ extern "C" int ag_gemm_ex(const void* const* shards, int32_t N, int64_t M, int64
     const int64_t H = M / N;
     const int64_t S = (H + comm_block_rows - 1) / comm_block_rows;
     const int64_t nchunks = (int64_t)N * S;
+    const bool in_fp8 = opt && opt->in_dtype == AG_IN_FP8_E4M3;
+    const int64_t esize = in_fp8 ? 1 : 2;   // bytes per element of the shards, B and A
     void* a_buf = opt ? opt->a_out : nullptr;
     if (!a_buf && K > 0) {
-        if ((rc = ensure_a(*w, (size_t)M * K * 2)) != AG_OK)
+        if ((rc = ensure_a(*w, (size_t)(M * K * esize))) != AG_OK)
             return rc;
         a_buf = w->a_agg;
     }
@@ -275,7 +281,8 @@ extern "C" int ag_gemm_ex(const void* const* shards, int32_t N, int64_t M, int64
     g.reverse_order = opt ? opt->reverse_order : 0;
     g.wait_stats = opt ? static_cast<uint64_t*>(opt->wait_stats) : nullptr;
     g.out_fp8 = (opt && opt->out_dtype == AG_OUT_FP8_E4M3) ? 1 : 0;
-    g.out_scale = (opt && opt->out_scale != 0.0f) ? opt->out_scale : 1.0f;
+    g.in_fp8 = in_fp8 ? 1 : 0;
+    g.out_scale = ((g.out_fp8 || g.in_fp8) && opt->out_scale != 0.0f) ? opt->out_scale : 1.0f;
 
     if (K == 0) {
         // empty reduction: C = 0, nothing to gather
@@ -295,7 +302,7 @@ extern "C" int ag_gemm_ex(const void* const* shards, int32_t N, int64_t M, int64
             d.src[r] = shards[r];
         d.dst = a_buf;
         d.nranks = N;
-        d.elem_size = 2;
+        d.elem_size = (int)esize;
         d.planes = 1;
         d.H = H;
         d.W = K;
@@ -346,15 +353,15 @@ extern "C" int ag_gemm_ex(const void* const* shards, int32_t N, int64_t M, int64
         AG_HIP(hipStreamWaitEvent(w->side, w->fork, 0), "hipStreamWaitEvent(side)");
         if ((rc = gemm_timed(g, kGemmFused, nullptr, s, opt)) != AG_OK)
             return rc;
-        const PieceMap pm = pm_make(H, comm_block_rows, N, g.local_rank, K, gemm_tile_m(), 1);
+        const PieceMap pm = pm_make(H, comm_block_rows, N, g.local_rank, K * esize, gemm_tile_m(), 1);
         for (int64_t pos = 0; pos < pm.nchunks; ++pos) {
             const int64_t c = pm_ready_chunk(pm, pos);
             int64_t first = 0, last = 0;
             pm_chunk_rows(pm, c, first, last);
             const int64_t r = c / pm.S;
-            const char* src = static_cast<const char*>(shards[r]) + (first - r * H) * K * 2;
-            char* dst = static_cast<char*>(a_buf) + first * K * 2;
-            AG_HIP(hipMemcpyAsync(dst, src, (size_t)((last - first) * K * 2), hipMemcpyDeviceToDeviceNoCU,
+            const char* src = static_cast<const char*>(shards[r]) + (first - r * H) * K * esize;
+            char* dst = static_cast<char*>(a_buf) + first * K * esize;
+            AG_HIP(hipMemcpyAsync(dst, src, (size_t)((last - first) * K * esize), hipMemcpyDeviceToDeviceNoCU,
                                   w->side), "hipMemcpyAsync(copy engine)");
             AG_HIP(hipStreamWriteValue32(w->side, w->flags + c, g.epoch, 0), "hipStreamWriteValue32(flag)");
         }

@@ -28,7 +28,8 @@
 // K step 64, v_mfma_f32_32x32x16_bf16, A/B tiles staged in LDS by buffer_load ... lds (16 B per
 // lane, no VGPR round trip), double-buffered (2 x 64 KiB).  LDS rows are 128 B (64 bf16) and
 // their 16-byte chunks are XOR-swizzled so the ds_read_b128 fragment loads are conflict-free
-// (every bank serves at most four dwords of a wave's read).
+// (every bank serves at most four dwords of a wave's read).  FP8 inputs keep the same 128-byte
+// rows (K step 128) and use v_mfma_f32_32x32x64_f8f6f4: a lane's fragment is two 16-byte chunks.
 #include "ag_device.hpp"
 #include "ag_internal.hpp"
 #include "ag_protocol.hpp"
@@ -38,7 +39,9 @@
 namespace ag {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 64;
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int BM = 256, BN = 256, BK = 64;     // BK: bf16 elements per K step (128 bytes)
 constexpr int NT = 256;                        // threads per workgroup
 constexpr int SLOTS = BM * BK * 2 / 16;        // 16-byte slots per operand tile (2048)
 constexpr int TILE_BYTES = SLOTS * 16;         // 32 KiB per operand tile
@@ -445,7 +448,7 @@ __device__ void drain_pieces(const KParams& p, uint32_t* ctr, int64_t end, int t
 // The GEMM itself; MODE plain or fused.  TRICKLE: the running waves' background copy is compiled in
 // (in-kernel producer only).  Idle, its bookkeeping still costs a few percent of the K loop, so
 // every other schedule runs without it.
-template <int MODE, bool TRICKLE>
+template <int MODE, bool TRICKLE, bool F8>
 __device__ __forceinline__ void gemm_body(KParams p)
 {
     __shared__ __attribute__((aligned(1024))) char sA0[TILE_BYTES];
@@ -467,26 +470,35 @@ __device__ __forceinline__ void gemm_body(KParams p)
     // contiguous run of tile ids (neighbouring tiles share A rows / B rows in that XCD's L2).
     const int vid = (G % 8 == 0) ? (int)(blockIdx.x % 8) * (G / 8) + (int)(blockIdx.x / 8) : (int)blockIdx.x;
     const int64_t num_tiles = (int64_t)p.num_pid_m * p.num_pid_n;
+    // A K step is one 128-byte row segment per operand row: 64 bf16 or 128 FP8 elements.
     const int64_t K = a.K;
-    const int64_t nk = (K + BK - 1) / BK;
+    const int64_t KB = F8 ? K : K * 2;             // bytes per row of A and B
+    const int64_t nk = (KB + 127) / 128;
     const int64_t lo = (int64_t)a.local_rank * a.H, hi = lo + a.H;
 
     // per-thread constants of the global->LDS copy: slot t of every 256-slot block
     const uint32_t r_in = tid >> 3;                  // row within a 32-row block
     const uint32_t cchunk = (tid & 7) ^ swz(r_in);   // logical 16-byte chunk this slot holds
-    const uint32_t row_stride32 = (uint32_t)(32 * K * 2);
-    const uint32_t voff0 = r_in * (uint32_t)(K * 2) + cchunk * 16;
+    const uint32_t row_stride32 = (uint32_t)(32 * KB);
+    const uint32_t voff0 = r_in * (uint32_t)KB + cchunk * 16;
+    const int32_t kval_lim = (int32_t)KB - (int32_t)cchunk * 16;   // this slot's chunk is in the row
+                                                                    // in K steps kb * 128 < kval_lim
     const uint32_t lds_wave_off = wave * 1024;
 
-    // per-lane constants of the LDS->VGPR fragment reads
+    // per-lane constants of the LDS->VGPR fragment reads.  bf16: substep kk (16 k) reads chunk
+    // 2 kk + fh of its row.  FP8: substep kk (64 k) reads chunks 4 kk + 2 fh and the one after it,
+    // at a_off[2 kk] and a_off[2 kk + 1] (A and B fragments take the k values in the same lane
+    // order, so the dot products are those of A and B's rows whatever order the instruction sums
+    // them in).
     const uint32_t fr = lane & 31, fh = lane >> 5;
     const uint32_t fsw = swz(fr & 15);
     uint32_t a_off[4], b_off[4];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        const uint32_t phys = ((uint32_t)(2 * kk) + fh) ^ fsw;
-        a_off[kk] = (wm * 128 + fr) * 128 + phys * 16;
-        b_off[kk] = (wn * 128 + fr) * 128 + phys * 16;
+    for (int q = 0; q < 4; ++q) {
+        const uint32_t chunk = F8 ? (uint32_t)(4 * (q >> 1) + (q & 1)) + 2 * fh : (uint32_t)(2 * q) + fh;
+        const uint32_t phys = chunk ^ fsw;
+        a_off[q] = (wm * 128 + fr) * 128 + phys * 16;
+        b_off[q] = (wn * 128 + fr) * 128 + phys * 16;
     }
 
     bool exhausted = false;   // (wave 0) no piece left to claim in this call
@@ -510,7 +522,7 @@ __device__ __forceinline__ void gemm_body(KParams p)
         const char* a_base;
         int64_t a_rows;
         if (MODE == kGemmFused && tc.m0 >= lo && m1 <= hi) {
-            a_base = static_cast<const char*>(a.shards[a.local_rank]) + (tc.m0 - lo) * K * 2;
+            a_base = static_cast<const char*>(a.shards[a.local_rank]) + (tc.m0 - lo) * KB;
             a_rows = m1 - tc.m0;
         } else {
             if (MODE == kGemmFused) {
@@ -525,7 +537,7 @@ __device__ __forceinline__ void gemm_body(KParams p)
                         s_ws.skipped += 1;
                 }
             }
-            a_base = static_cast<const char*>(a.A) + tc.m0 * K * 2;
+            a_base = static_cast<const char*>(a.A) + tc.m0 * KB;
             a_rows = m1 - tc.m0;
         }
         if (MODE == kGemmFused && wave0) {
@@ -539,9 +551,9 @@ __device__ __forceinline__ void gemm_body(KParams p)
             }
         }
         const int64_t b_rows = min((int64_t)BN, a.Nc - tc.n0);
-        const char* b_base = static_cast<const char*>(a.B) + tc.n0 * K * 2;
-        const uint32_t a_bytes = (uint32_t)(a_rows * K * 2);
-        const uint32_t b_bytes = (uint32_t)(b_rows * K * 2);
+        const char* b_base = static_cast<const char*>(a.B) + tc.n0 * KB;
+        const uint32_t a_bytes = (uint32_t)(a_rows * KB);
+        const uint32_t b_bytes = (uint32_t)(b_rows * KB);
 
         f32x16 acc[4][4];
 #pragma unroll
@@ -552,13 +564,11 @@ __device__ __forceinline__ void gemm_body(KParams p)
                 for (int v = 0; v < 16; ++v)
                     acc[i][j][v] = 0.0f;
 
-        // Loads of K step kb into one stage.  The resource is re-based by kb*BK elements and shrunk
-        // by as many bytes, so rows past the tile's valid rows read zeros; a chunk past K reads
-        // zeros through an out-of-range offset.
         // Loads of K step kb into one stage: 8 + 8 DMA operations of 16 bytes per lane.  The
-        // resource is re-based by kb*BK elements and shrunk by as many bytes, so rows past the
-        // tile's valid rows read zeros; a 16-byte chunk past K starts its offsets at the tile's full
-        // byte size, at or beyond this step's resource size, so it reads zeros (no branch per lane).
+        // resource is re-based by the step's 128 bytes per row and shrunk by as many, so rows past
+        // the tile's valid rows read zeros; a 16-byte chunk past the row's end starts its offsets at
+        // the tile's full byte size, at or beyond this step's resource size, so it reads zeros (no
+        // branch per lane).
         // The 16 LDS destinations and row offsets of a stage are rebuilt from the wave's LDS offset
         // and the row stride at every K step (one scalar op each): left to itself the compiler
         // keeps all of them in scalar registers for the whole kernel, and with the fused
@@ -575,10 +585,10 @@ __device__ __forceinline__ void gemm_body(KParams p)
             d.lw = lds_wave_off;
             d.rs = row_stride32;
             asm volatile("" : "+s"(d.lw), "+s"(d.rs));
-            const uint32_t kbyte = (uint32_t)(kb * BK * 2);
+            const uint32_t kbyte = (uint32_t)(kb * 128);
             d.ra = make_rsrc(a_base + kbyte, a_bytes - kbyte);
             d.rb = make_rsrc(b_base + kbyte, b_bytes - kbyte);
-            const bool kval = (int64_t)kb * BK + cchunk * 8 < K;
+            const bool kval = (int32_t)(kb * 128) < kval_lim;
             d.va = kval ? voff0 : a_bytes;
             d.vb = kval ? voff0 : b_bytes;
             d.sa = sa;
@@ -630,7 +640,7 @@ __device__ __forceinline__ void gemm_body(KParams p)
         // One K step out of stage (sa, sb) while the loads of the next step fill the other stage:
         // all 16 DMA operations go out during the first two substeps, which leaves the last two
         // (1024 MFMA cycles) for them to land before the next barrier.
-        auto compute = [&](const char* sa, const char* sb, const Dma& d) {
+        auto compute_bf16 = [&](const char* sa, const char* sb, const Dma& d) {
             bf16x8 a0[4], b0[4], a1[4], b1[4];
             load_frags(sa, sb, 0, a0, b0);
             load_frags(sa, sb, 1, a1, b1);
@@ -647,6 +657,59 @@ __device__ __forceinline__ void gemm_body(KParams p)
             __builtin_amdgcn_sched_barrier(0);
             mfma_block(a1, b1, d, 0, 0);
             __builtin_amdgcn_sched_barrier(0);
+        };
+        // FP8: a lane's fragment of substep kk is its row's 32 bytes at k bytes [64 kk + 32 fh, +32),
+        // two chunks; a K step is two substeps of 16 v_mfma_f32_32x32x64_f8f6f4 (E4M3 operands: both
+        // format fields 0; no block scales), in rows i of four MFMAs that share A fragment i.  The
+        // B fragments of both substeps stay in registers; the A fragments stream, each read one row
+        // of MFMAs ahead (80 VGPRs of fragments instead of 128, which keeps the fused kernel within
+        // the VGPR budget it shares with the copy kernel beside it).  The 16 DMA operations of the
+        // next stage go out one per MFMA of the first substep -- the same spacing in time as the
+        // bf16 step's -- which leaves the second substep for them to land.
+        auto frag8 = [&](const char* base, const uint32_t* off, int kk, int i) {
+            const i32x4 x = *reinterpret_cast<const i32x4*>(base + off[2 * kk] + i * 4096);
+            const i32x4 y = *reinterpret_cast<const i32x4*>(base + off[2 * kk + 1] + i * 4096);
+            return __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
+        };
+        auto compute_f8 = [&](const char* sa, const char* sb, const Dma& d) {
+            i32x8 b0[4], b1[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                b0[j] = frag8(sb, b_off, 0, j);
+            i32x8 ac = frag8(sa, a_off, 0, 0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                b1[j] = frag8(sb, b_off, 1, j);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int st = 0; st < 2; ++st) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bool more = st == 0 || i < 3;
+                    i32x8 an = ac;
+                    if (more)
+                        an = frag8(sa, a_off, i < 3 ? st : 1, i < 3 ? i + 1 : 0);
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(st == 0 ? b0[j] : b1[j], ac,
+                                                                                    acc[i][j], 0, 0, 0, 0, 0, 0);
+                        if (st == 0) {
+                            __builtin_amdgcn_sched_barrier(0);
+                            dma_op(d, 4 * i + j);
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    ac = an;
+                }
+            }
+        };
+        auto compute = [&](const char* sa, const char* sb, const Dma& d) {
+            if constexpr (F8)
+                compute_f8(sa, sb, d);
+            else
+                compute_bf16(sa, sb, d);
         };
 
         // Double-buffered K loop.  With an odd number of K steps the first one runs alone out of
@@ -743,14 +806,23 @@ __device__ __forceinline__ void gemm_body(KParams p)
                         continue;
                     }
                     bf16x8 o;
-                    o[0] = (__bf16)x0[0];
-                    o[1] = (__bf16)x0[1];
-                    o[2] = (__bf16)x0[2];
-                    o[3] = (__bf16)x0[3];
-                    o[4] = (__bf16)x1[0];
-                    o[5] = (__bf16)x1[1];
-                    o[6] = (__bf16)x1[2];
-                    o[7] = (__bf16)x1[3];
+                    if constexpr (F8) {
+                        // FP8 inputs: the caller's per-tensor scales come in as out_scale
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            o[e] = (__bf16)(x0[e] * scale);
+                            o[4 + e] = (__bf16)(x1[e] * scale);
+                        }
+                    } else {
+                        o[0] = (__bf16)x0[0];
+                        o[1] = (__bf16)x0[1];
+                        o[2] = (__bf16)x0[2];
+                        o[3] = (__bf16)x0[3];
+                        o[4] = (__bf16)x1[0];
+                        o[5] = (__bf16)x1[1];
+                        o[6] = (__bf16)x1[2];
+                        o[7] = (__bf16)x1[3];
+                    }
                     if (publish) {
                         const __amdgpu_buffer_rsrc_t rc =
                             make_rsrc(C + (wrow0 + i * 32) * a.Nc + wcol0, (uint32_t)(32 * a.Nc * 2));
@@ -810,7 +882,12 @@ __device__ __forceinline__ void gemm_body(KParams p)
 // The kernels.  KParams is each one's first (only) argument, which kparams() relies on.
 __global__ __launch_bounds__(NT, 1) void gemm_plain_kernel(KParams p)
 {
-    gemm_body<kGemmPlain, false>(p);
+    gemm_body<kGemmPlain, false, false>(p);
+}
+
+__global__ __launch_bounds__(NT, 1) void gemm_plain_f8_kernel(KParams p)
+{
+    gemm_body<kGemmPlain, false, true>(p);
 }
 
 // The fused kernels run beside other work on every CU -- the side-stream copy kernel, the runtime's
@@ -820,12 +897,22 @@ __global__ __launch_bounds__(NT, 1) void gemm_plain_kernel(KParams p)
 // room those kernels cannot start until the GEMM ends, while the GEMM waits for them.
 __global__ __launch_bounds__(NT, 1) void gemm_fused_kernel(KParams p)
 {
-    gemm_body<kGemmFused, false>(p);
+    gemm_body<kGemmFused, false, false>(p);
 }
 
 __global__ __launch_bounds__(NT, 1) void gemm_fused_trickle_kernel(KParams p)
 {
-    gemm_body<kGemmFused, true>(p);
+    gemm_body<kGemmFused, true, false>(p);
+}
+
+__global__ __launch_bounds__(NT, 1) void gemm_fused_f8_kernel(KParams p)
+{
+    gemm_body<kGemmFused, false, true>(p);
+}
+
+__global__ __launch_bounds__(NT, 1) void gemm_fused_trickle_f8_kernel(KParams p)
+{
+    gemm_body<kGemmFused, true, true>(p);
 }
 
 // Copy kernel of the side-stream schedule, beside the GEMM.  It is small -- no LDS tile, few VGPRs --
@@ -925,10 +1012,11 @@ KParams make_params(const GemmArgs& a, GemmMode mode)
     p.npieces = 0;
     p.fill_end = 0;
     p.trickle = 0;
-    p.pm = pm_make(1, 1, 1, 0, a.K, BM, PIECE_BYTES);
+    const int64_t row_bytes = a.in_fp8 ? a.K : a.K * 2;
+    p.pm = pm_make(1, 1, 1, 0, row_bytes, BM, PIECE_BYTES);
     if (mode == kGemmFused) {
         p.pivot = (int)(((int64_t)a.local_rank * a.H) / BM % p.num_pid_m);
-        p.pm = pm_make(a.H, a.cb, a.nshards, a.local_rank, a.K, BM, PIECE_BYTES);
+        p.pm = pm_make(a.H, a.cb, a.nshards, a.local_rank, row_bytes, BM, PIECE_BYTES);
         p.npieces = a.copy_pieces ? p.pm.nchunks * p.pm.ppc : 0;
         p.trickle = a.copy_pieces == 1 ? 1 : 0;
     } else if (a.tile_done) {
@@ -1031,13 +1119,14 @@ hipError_t launch_gemm(const GemmArgs& a, GemmMode mode, const FusedPlan* f, hip
     if (f)
         p.fill_end = f->fill_end;
     const int grid = gemm_grid(p, cus);
-    if (mode == kGemmFused)
+    if (mode == kGemmFused) {
         if (p.trickle)
-            gemm_fused_trickle_kernel<<<grid, NT, 0, stream>>>(p);
+            (a.in_fp8 ? gemm_fused_trickle_f8_kernel : gemm_fused_trickle_kernel)<<<grid, NT, 0, stream>>>(p);
         else
-            gemm_fused_kernel<<<grid, NT, 0, stream>>>(p);
-    else
-        gemm_plain_kernel<<<grid, NT, 0, stream>>>(p);
+            (a.in_fp8 ? gemm_fused_f8_kernel : gemm_fused_kernel)<<<grid, NT, 0, stream>>>(p);
+    } else {
+        (a.in_fp8 ? gemm_plain_f8_kernel : gemm_plain_kernel)<<<grid, NT, 0, stream>>>(p);
+    }
     return hipGetLastError();
 }
 

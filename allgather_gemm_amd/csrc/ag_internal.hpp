@@ -53,7 +53,8 @@ struct GemmArgs {
     int reverse_order;      // stress: hand pieces out back to front
     int64_t spin_limit;     // 100 MHz ticks of one flag wait before giving up
     int out_fp8;            // C is FP8 E4M3 "fn" bytes (else bf16)
-    float out_scale;        // FP8 output: C = e4m3fn(acc * out_scale)
+    int in_fp8;             // A, B and the shards are FP8 E4M3 "fn" codes (else bf16)
+    float out_scale;        // C = convert(acc * out_scale) with FP8 output or FP8 inputs (else 1)
     // GEMM + ReduceScatter (plain mode): tiles holding rows [pub_lo, pub_hi) of C store them
     // write-through and then count themselves in tile_done[tile row - pub_lo / BM]; the tile walk
     // starts at pub_lo.  nullptr: no publishing.

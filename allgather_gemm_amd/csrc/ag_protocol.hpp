@@ -33,7 +33,7 @@ struct PieceMap {
     int64_t H;            // rows per shard
     int64_t cb;           // rows per chunk
     int64_t S;            // chunks per shard
-    int64_t row_bytes;    // K * 2
+    int64_t row_bytes;    // K * element size
     int64_t piece_bytes;  // bytes per piece (multiple of 16)
     int64_t ppc;          // pieces per chunk
     int64_t nchunks;      // nshards * S
@@ -62,14 +62,14 @@ AG_HD void pm_local_chunks_meeting(const PieceMap& p, int64_t r0, int64_t r1, in
 
 // Fills the map.  bm: GEMM tile rows (the edge chunks are those meeting the tile rows that hold the
 // local shard's first and last row, when those tiles also hold rows of another shard).
-AG_HD PieceMap pm_make(int64_t H, int64_t cb, int32_t nshards, int32_t local, int64_t K, int64_t bm,
-                       int64_t piece_bytes)
+AG_HD PieceMap pm_make(int64_t H, int64_t cb, int32_t nshards, int32_t local, int64_t row_bytes,
+                       int64_t bm, int64_t piece_bytes)
 {
     PieceMap p;
     p.H = H;
     p.cb = cb;
     p.S = (H + cb - 1) / cb;
-    p.row_bytes = K * 2;
+    p.row_bytes = row_bytes;
     p.piece_bytes = piece_bytes;
     const int64_t chunk_bytes = cb * p.row_bytes;
     p.ppc = chunk_bytes > 0 ? (chunk_bytes + piece_bytes - 1) / piece_bytes : 1;

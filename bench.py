@@ -12,10 +12,12 @@ Besides the headline the JSON line carries, per the fused AllGather+MatMul artic
 (section 性能结果与适用边界: warm-up, statistic, baseline, effective bandwidth, utilisation):
   * every schedule of the square workload -- fused with each producer, unfused (gather, then GEMM),
     GEMM-only (flags raised beforehand) and the plain GEMM alone -- as median / p10 / p90 of
-    individually timed calls, cold (a 1 GiB write evicts L2 and the MALL before every call) and hot;
+    individually timed calls, cold (a 1 GiB read evicts L2 and the MALL before every call) and hot;
   * the MLP-up (16384 x 14336 x 4096) and ragged (4000 x 28672 x 8192) workloads the same way;
   * GEMM + ReduceScatter (one rank's share of the square workload split over 8 ranks), fused and
     serial;
+  * FP8 inputs (E4M3 A and B, bf16 C) on the square workload, its schedules as above, the GEMM
+    kernel against the 5 PFLOP/s dense fp8 peak;
   * TGATHER on its two workloads, cold and hot, as GB/s of algorithmic traffic;
   * the shader clock sampled while fused calls run back to back;
   * the CPU oracle timed on a bounded sample of the square workload.
@@ -24,12 +26,14 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--reps R] [--no-cpu-
        python bench.py --headline-only ...   (headline steps only, for kernel traces and counters)
        python bench.py --tgather-only ...    (TGATHER workloads only, likewise)
        python bench.py --rs-only ...         (GEMM + ReduceScatter only, likewise)
+       python bench.py --fp8-only ...        (FP8-input square workload only, likewise)
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
 import json
+import math
 import os
 import re
 import shutil
@@ -43,6 +47,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "AG-GEMM bf16 TFLOP/s + gather GB/s (% of peak), fused vs unfused speedup"
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+PEAK_FP8_TFLOPS = 5000.0       # MI355X dense fp8 MFMA, published
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_FLOPS_PER_CLK = 256 * 4 * 1024   # CUs x SIMDs x dense bf16 flops per SIMD per clock
 PROFILES = os.path.join(ROOT, "profiles")
@@ -62,6 +67,8 @@ def parse():
                     help="only the headline steps (plus one calibration copy): for rocprofv3 runs")
     ap.add_argument("--tgather-only", action="store_true",
                     help="only TGATHER on its two workloads, --steps calls each: for rocprofv3 runs")
+    ap.add_argument("--fp8-only", action="store_true",
+                    help="only the FP8-input square workload, --steps fused calls: for rocprofv3 runs")
     ap.add_argument("--rs-only", action="store_true",
                     help="only GEMM + ReduceScatter, --steps fused then --steps serial calls: for rocprofv3 runs")
     return ap.parse_args()
@@ -255,6 +262,39 @@ def main():
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
 
+    def fp8_inputs():
+        fcfg = workloads.AG_SQUARE_FP8
+        fA, fsh, fB = workloads.make_ag_gemm_fp8(fcfg)
+        fsd = [t.to(dev) for t in fsh]
+        fBd = fB.to(dev)
+        fC = torch.empty((fcfg.M, fcfg.Nc), dtype=torch.bfloat16, device=dev)
+        fa = torch.empty((fcfg.M, fcfg.K), dtype=torch.uint8, device=dev)
+        fkw = {"in_dtype": "fp8_e4m3", "out_scale": 1.0 / math.sqrt(fcfg.K)}
+        torch.cuda.synchronize()
+        return fcfg, fsd, fBd, fC, fa, fkw
+
+    if args.fp8_only:
+        fcfg, fsd, fBd, fC, fa, fkw = fp8_inputs()
+        kev8 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+        for k in kev8:      # torch creates an event when it first records it
+            k[0].record(stream)
+            k[1].record(stream)
+        for _ in range(args.warmup):
+            ag.ag_gemm(fsd, fBd, fcfg.cb, C=fC, a_out=fa, **fkw)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            ag.ag_gemm(fsd, fBd, fcfg.cb, C=fC, a_out=fa, gemm_events=kev8[i], **fkw)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        kms = sum(k[0].elapsed_time(k[1]) for k in kev8) / args.steps
+        print(json.dumps({"fp8_only": True, "workload": fcfg.name, "ms_per_step": round(ms, 5),
+                          "gemm_kernel_ms": round(kms, 5),
+                          "kernel_TFLOP/s": round(fcfg.flops / (kms * 1e-3) / 1e12, 2)}), flush=True)
+        return
+
     if args.rs_only:
         rcfg = workloads.RS_SQUARE
         rA, rB, rrecv = workloads.make_gemm_rs(rcfg)
@@ -424,6 +464,20 @@ def main():
         del osd, oBd, oC, oa
         torch.cuda.empty_cache()
 
+    # FP8 inputs on the square workload: E4M3 A and B, bf16 C = A B^T / sqrt(K)
+    fcfg, fsd, fBd, fC, fa, fkw = fp8_inputs()
+    ag.ag_gemm(fsd, fBd, fcfg.cb, C=fC, a_out=fa, mode="unfused", **fkw)
+    fp8_in = schedule_stats(fcfg, fsd, fBd, fC, fa, [(n, {**kw, **fkw}) for n, kw in modes_o])
+    for name in ("fused", "unfused", "gemm_only", "plain_gemm"):
+        kms = fp8_in[name]["gemm_kernel_hot_median_ms"]
+        fp8_in[name]["gemm_kernel_hot_tflops"] = round(fcfg.flops / (kms * 1e-3) / 1e12, 2)
+        fp8_in[name]["gemm_kernel_hot_frac_of_fp8_peak"] = round(fcfg.flops / (kms * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)
+    fp8_in["config"] = {"workload": fcfg.name, "M": fcfg.M, "K": fcfg.K, "Nc": fcfg.Nc, "shards": fcfg.N,
+                        "comm_block_rows": fcfg.cb, "inputs": "fp8_e4m3", "C": "bf16",
+                        "out_scale": fkw["out_scale"], "peak_tflops": PEAK_FP8_TFLOPS}
+    del fsd, fBd, fC, fa
+    torch.cuda.empty_cache()
+
     # GEMM + ReduceScatter, one rank's share, on the square workload split over 8 ranks
     rcfg = workloads.RS_SQUARE
     rA, rB, rrecv = workloads.make_gemm_rs(rcfg)
@@ -498,6 +552,7 @@ def main():
         "workloads": other,
         "tgather": gathers,
         "gemm_reduce_scatter": rs,
+        "fp8_inputs": fp8_in,
         "sclk": sclk,
         "protocol": {"reps": reps, "warmup_per_statistic": warm,
                      "cold": "1 GiB read (torch amax) before every timed call", "statistic": "median, p10, p90"},

@@ -63,10 +63,19 @@ extern "C" {
                                  rounded to nearest even; NaN where that lands beyond +-448
                                  ([AGMM] MatMul 按需等待: the MatMul's FP8_OUTPUT variant) */
 
+/* Element type of the shards, B and the gathered A (ag_options.in_dtype). */
+#define AG_IN_BF16       0    /* bf16 (default) */
+#define AG_IN_FP8_E4M3   1    /* FP8 E4M3 "fn" codes, one byte per element (K % 16 == 0).  Every
+                                 product of two such values is exact in fp32 and the sums run in
+                                 fp32, as for bf16; per-tensor scales of A and B fold into
+                                 out_scale.  An extension of [AGMM]'s FP8 variant (there only the
+                                 output is FP8) onto gfx950's FP8 matrix instructions. */
+
 typedef struct ag_options {
     int32_t mode;          /* AG_MODE_* */
     int32_t local_rank;    /* shard whose rows the rotated tile walk starts at, 0..N-1 */
-    void *a_out;           /* NULL, or an (M, K) bf16 device buffer that receives the gathered A.
+    void *a_out;           /* NULL, or an (M, K) device buffer (of the input element type) that
+                              receives the gathered A.
                               Required for AG_MODE_GEMM_ONLY and AG_MODE_PLAIN_GEMM, where it must
                               already hold it. */
     int64_t timeout_us;    /* give-up time of one flag wait, microseconds (<= 0: 10 s) */
@@ -86,6 +95,9 @@ typedef struct ag_options {
                               GEMM adds to: 100 MHz clock ticks its workgroups spent waiting on chunk
                               flags (summed over workgroups), waits, pieces copied by waiting
                               workgroups, tiles that skipped their wait (flags read in advance) */
+    int32_t in_dtype;      /* AG_IN_*; with AG_IN_FP8_E4M3 the shards, B and a_out hold one byte per
+                              element, and C = out_scale * (A B^T) in bf16 or (out_dtype) FP8 --
+                              out_scale then applies to bf16 output too (0 means 1) */
 } ag_options;
 
 /*
@@ -126,8 +138,8 @@ int ag_gemm_ex(const void *const *shards, int32_t N, int64_t M, int64_t K, const
  *                        do not divide H / W; values above H / W mean one tile spans the plane.
  *                        The result does not depend on them (a copy is exact); the work split does.
  *   elem_size            1, 2, 4 or 8 bytes.
- * Any extent of 0 enqueues nothing ([TGATH] 7.4).  16-byte aligned pointers with
- * W * elem_size % 16 == 0 take the LDS-staged 16-byte path; anything else a slower element path.
+  * Any extent of 0 enqueues nothing ([TGATH] 7.4).  16-byte aligned pointers with
+ * W * elem_size % 16 == 0 take the 16-byte vector path; anything else a slower element path.
  */
 int tgather(const void *const *shards, int32_t N, void *dst, int64_t D0, int64_t D1, int64_t D2,
             int64_t H, int64_t W, int64_t valid_rows, int64_t valid_cols, int32_t elem_size,

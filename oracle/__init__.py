@@ -54,6 +54,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_f32_to_e4m3fn.restype = ctypes.c_uint8
         L.oracle_e4m3fn_value.argtypes = [ctypes.c_uint8]
         L.oracle_e4m3fn_value.restype = ctypes.c_double
+        L.oracle_e4m3fn_to_bf16.argtypes = [_vp, _i64, _vp]
+        L.oracle_e4m3fn_to_bf16.restype = ctypes.c_int
         L.oracle_tgather.argtypes = [_vp, ctypes.c_int, _vp, _i64, _i64, _i64, _i64, _i64, _i64,
                                      ctypes.c_int]
         L.oracle_tgather.restype = ctypes.c_int
@@ -148,6 +150,16 @@ def e4m3fn_value(codes) -> np.ndarray:
     cs = np.asarray(codes, dtype=np.uint8)
     f = lib().oracle_e4m3fn_value
     return np.array([f(int(c)) for c in cs.ravel()], dtype=np.float64).reshape(cs.shape)
+
+
+def e4m3fn_to_bf16(codes) -> np.ndarray:
+    """bf16 bit patterns (uint16) of E4M3 "fn" codes' values, exact (see oracle.h).  The GEMM of FP8
+    inputs is gemm_f32 / ag_gemm_at on these patterns."""
+    cs = np.ascontiguousarray(codes, dtype=np.uint8)
+    out = np.empty(cs.shape, dtype=np.uint16)
+    if lib().oracle_e4m3fn_to_bf16(_ptr(cs), cs.size, _ptr(out)) != 0:
+        raise ValueError("an E4M3 value was not exactly a bf16 value")
+    return out
 
 
 def tgather(shards, dst: np.ndarray, D0: int, D1: int, D2: int, H: int, W: int,

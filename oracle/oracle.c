@@ -104,6 +104,23 @@ double oracle_e4m3fn_value(uint8_t code)
     return s * ldexp(8.0 + mant, field - 10);
 }
 
+/* FP8 inputs: the bf16 bit pattern of an E4M3 "fn" code's value.  Every finite E4M3 value has a
+ * 4-bit significand and an exponent in [-9, 8], so it is exactly a bf16 value (8-bit significand,
+ * bf16's exponent range): the pattern is the top half of the value's float pattern, whose bottom
+ * half is zero.  S.1111.111 becomes a bf16 NaN.  Returns -1 if a finite value were not exact. */
+int oracle_e4m3fn_to_bf16(const uint8_t *codes, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        const float v = (float)oracle_e4m3fn_value(codes[i]);
+        uint32_t u;
+        memcpy(&u, &v, 4);
+        if (!isnan(v) && (u & 0xFFFFu) != 0)
+            return -1;
+        out[i] = (uint16_t)(u >> 16);
+    }
+    return 0;
+}
+
 /* [TGATH] §二 数学语义 (closed form), §7.2 内存约束 (taller dst keeps its extra rows),
  * §7.4 (empty data moves nothing), §6.3 CPU_SIM (element copy semantics). */
 int oracle_tgather(const void *const *src, int nranks, void *dst,

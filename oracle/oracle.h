@@ -51,6 +51,13 @@ void oracle_reduce_block(const uint16_t *const *parts, int nparts, int64_t H, in
 uint8_t oracle_f32_to_e4m3fn(float x);
 /* The value an E4M3 "fn" code stands for (NaN for S.1111.111). */
 double oracle_e4m3fn_value(uint8_t code);
+/*
+ * FP8 inputs (an extension of the FP8 variant above onto the inputs): every finite E4M3 "fn" value
+ * is exactly a bf16 value, so A and B in E4M3 are multiplied as the bf16 GEMM does, on the bf16
+ * images of their codes: exact products, fp32 sums in ascending k.  This gives those images
+ * (NaN code -> bf16 NaN); returns -1 if a finite value were not exactly representable.
+ */
+int oracle_e4m3fn_to_bf16(const uint8_t *codes, int64_t n, uint16_t *out);
 
 /*
  * TGATHER closed form, [TGATH] §二 数学语义:

@@ -254,7 +254,7 @@ int main(int argc, char** argv)
     m.slice = std::atoll(argv[12]);
     const unsigned seed = (unsigned)std::atoi(argv[13]);
     m.M = m.N * m.H;
-    m.pm = pm_make(m.H, m.cb, m.N, m.local, m.K, m.bm, piece_bytes);
+    m.pm = pm_make(m.H, m.cb, m.N, m.local, m.K * 2, m.bm, piece_bytes);   // K bf16 elements per row
     m.npieces = m.pm.nchunks * m.pm.ppc;
     m.num_pid_m = (m.M + m.bm - 1) / m.bm;
     m.num_pid_n = (m.Nc + m.bn - 1) / m.bn;

@@ -69,9 +69,17 @@ def test_ag_gemm_ex_rejects_bad_options():
                 ag.AgOptions(0, 0, None, 0, 0, 0, -1),
                 ag.AgOptions(0, 0, None, 0, 0, 0, 0, (_vp * 2)(None, None), 2, 1.0),   # unknown C type
                 ag.AgOptions(0, 0, None, 0, 0, 0, 0, (_vp * 2)(None, None), 1, float("inf")),
-                ag.AgOptions(0, 0, None, 0, 0, 0, 0, (_vp * 2)(None, None), 1, float("nan"))):
+                ag.AgOptions(0, 0, None, 0, 0, 0, 0, (_vp * 2)(None, None), 1, float("nan")),
+                ag.AgOptions(0, 0, None, 0, 0, 0, 0, (_vp * 2)(None, None), 0, 1.0, None, 2),   # unknown input type
+                ag.AgOptions(0, 0, None, 0, 0, 0, 0, (_vp * 2)(None, None), 0, 1.0, None, -1)):
         assert L.ag_gemm_ex(ptrs, 2, 8, 8, _vp(0x20000), 8, _vp(0x30000), 4, None,
                             ctypes.byref(opt)) == ag.AG_EINVAL
+    # FP8 inputs: rows must be whole 16-byte chunks (K % 16 == 0), which bf16 rows of K = 8 are
+    fp8 = ag.AgOptions(0, 0, None, 0, 0, 0, 0, (_vp * 2)(None, None), 0, 1.0, None, ag.IN_FP8_E4M3)
+    assert L.ag_gemm_ex(ptrs, 2, 8, 8, _vp(0x20000), 8, _vp(0x30000), 4, None,
+                        ctypes.byref(fp8)) == ag.AG_EINVAL
+    assert L.ag_gemm_ex(ptrs, 2, 8, 24, _vp(0x20000), 8, _vp(0x30000), 4, None,
+                        ctypes.byref(fp8)) == ag.AG_EINVAL
 
 
 def test_gemm_rs_rejects_bad_arguments():

@@ -390,6 +390,47 @@ def test_e4m3fn_matches_torch_float8_conversion():
     assert np.array_equal(ours, theirs), xs[ours != theirs][:10]
 
 
+# ------------------------------------------------------------------ FP8 inputs
+def test_e4m3fn_to_bf16_is_exact_for_every_code():
+    """Every E4M3 value's bf16 image is the same number: checked against torch's own float8_e4m3fn
+    decoding (an independent implementation), with the NaN code mapping to NaN."""
+    codes = np.arange(256, dtype=np.uint8)
+    bits = oracle.e4m3fn_to_bf16(codes)
+    as_f32 = (bits.astype(np.uint32) << 16).view(np.float32)
+    theirs = torch.from_numpy(codes).view(torch.float8_e4m3fn).float().numpy()
+    nan = np.isnan(theirs)
+    assert list(np.nonzero(nan)[0]) == [0x7F, 0xFF]
+    assert np.isnan(as_f32[nan]).all()
+    assert np.array_equal(as_f32[~nan], theirs[~nan])
+    assert np.array_equal(as_f32[~nan], oracle.e4m3fn_value(codes)[~nan].astype(np.float32))
+
+
+@pytest.mark.parametrize("M,Nc,K,seed", [(5, 7, 48, 1), (33, 17, 160, 2)])
+def test_fp8_input_gemm_exact_integers_against_int64(M, Nc, K, seed):
+    """FP8 integer inputs: the product through the bf16 images equals the int64 product."""
+    rng = np.random.default_rng(seed)
+    a = rng.integers(-4, 5, (M, K))
+    b = rng.integers(-4, 5, (Nc, K))
+    ca = torch.from_numpy(a.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    cb = torch.from_numpy(b.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    C = oracle.gemm_f32(oracle.e4m3fn_to_bf16(ca), oracle.e4m3fn_to_bf16(cb))
+    assert np.array_equal(C.astype(np.int64), a @ b.T)
+
+
+def test_fp8_input_gemm_within_fp32_bound_of_float64():
+    """Random E4M3 inputs: products are exact, so the fp32 ascending sum is within K * 2^-24 *
+    sum |a b| of the float64 product of the decoded values."""
+    rng = np.random.default_rng(7)
+    M, Nc, K = 9, 11, 320
+    ca = workloads.to_e4m3fn_codes(torch.from_numpy(rng.standard_normal((M, K)).astype(np.float32))).numpy()
+    cb = workloads.to_e4m3fn_codes(torch.from_numpy(rng.standard_normal((Nc, K)).astype(np.float32))).numpy()
+    va, vb = oracle.e4m3fn_value(ca), oracle.e4m3fn_value(cb)
+    C = oracle.gemm_f32(oracle.e4m3fn_to_bf16(ca), oracle.e4m3fn_to_bf16(cb)).astype(np.float64)
+    ref = va @ vb.T
+    bound = K * 2.0 ** -24 * (np.abs(va) @ np.abs(vb).T)
+    assert (np.abs(C - ref) <= bound).all()
+
+
 # ------------------------------------------------------------------ GEMM + ReduceScatter (one rank)
 def _int_bf16(rng, shape, lim):
     """Small integers as bf16 bit patterns (exact)."""

@@ -97,6 +97,38 @@ def make_ag_gemm_integers(N: int, H: int, K: int, Nc: int, seed: int = 0, lim: i
     return shards, B
 
 
+# FP8 inputs: the square workload with A and B in E4M3 "fn"; both ~ N(0, 1) before the conversion
+# (E4M3's normal range starts at 2^-6, so a weight spread of 0.02 would sit in its subnormals), and
+# the sums brought back to O(1) by out_scale = 1 / sqrt(K).
+AG_SQUARE_FP8 = AgGemmConfig("ag_gemm_8192x8192x8192_fp8", N=8, H=1024, K=8192, Nc=8192, cb=128,
+                             a_std=1.0, b_std=1.0)
+
+
+def to_e4m3fn_codes(x: torch.Tensor) -> torch.Tensor:
+    """uint8 E4M3 "fn" codes of fp32 values: torch's float8_e4m3fn conversion (round to nearest
+    even), viewed as bytes."""
+    return x.to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def make_ag_gemm_fp8(cfg: AgGemmConfig, seed: int | None = None):
+    """FP8 inputs: (A (M,K), shards [N x (H,K)], B (Nc,K)) as uint8 E4M3 codes, CPU tensors."""
+    g = torch.Generator().manual_seed(cfg.seed if seed is None else seed)
+    A = to_e4m3fn_codes(torch.randn(cfg.M, cfg.K, generator=g) * cfg.a_std)
+    B = to_e4m3fn_codes(torch.randn(cfg.Nc, cfg.K, generator=g) * cfg.b_std)
+    shards = [A[r * cfg.H:(r + 1) * cfg.H].contiguous() for r in range(cfg.N)]
+    return A, shards, B
+
+
+def make_ag_gemm_fp8_integers(N: int, H: int, K: int, Nc: int, seed: int = 0, lim: int = 4):
+    """FP8 inputs with integer values in [-lim, lim] (exact in E4M3 for lim <= 16): every fp32
+    partial sum is an integer below 2^24 for K * lim^2 < 2^24, exact in any order.  Returns
+    (shards, B) as uint8 codes."""
+    g = torch.Generator().manual_seed(seed)
+    shards = [to_e4m3fn_codes(torch.randint(-lim, lim + 1, (H, K), generator=g).float()) for _ in range(N)]
+    B = to_e4m3fn_codes(torch.randint(-lim, lim + 1, (Nc, K), generator=g).float())
+    return shards, B
+
+
 @dataclass(frozen=True)
 class GemmRsConfig:
     """One rank's GEMM + ReduceScatter: A (M, K) and B (Nc, K) are the rank's K slices; the other
