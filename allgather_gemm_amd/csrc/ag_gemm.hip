@@ -611,9 +611,7 @@ __device__ __forceinline__ void gemm_body(KParams p)
                 dma_op(d, q);
         };
 
-        // Fragments of two k-substeps in flight: the reads of substep kk+1 are issued before
-        // the 16 MFMAs of substep kk; sched_barrier keeps the compiler from hoisting further
-        // (which would cost 128 VGPRs on top of the 256 accumulators).
+        // Fragment reads of substep kk: four A and four B fragments, one ds_read_b128 each.
         auto load_frags = [&](const char* sa, const char* sb, int kk, bf16x8* af, bf16x8* bfr) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
@@ -622,48 +620,53 @@ __device__ __forceinline__ void gemm_body(KParams p)
             for (int j = 0; j < 4; ++j)
                 bfr[j] = *reinterpret_cast<const bf16x8*>(sb + b_off[kk] + j * 4096);
         };
-        // 16 MFMAs of one k-substep; with `ndma` > 0, DMA operations q0, q0+1, ... of the next
-        // stage go out between them (one per 16 / ndma MFMAs) instead of in one burst, so the
-        // texture path never backs up into this wave's instruction issue.
-        auto mfma_block = [&](const bf16x8* af, const bf16x8* bfr, const Dma& d, int q0, int ndma) {
+        // 16 MFMAs of one k-substep, and between them, one per two MFMAs: after odd ones the DMA
+        // operations q0, q0+1, ... of the next stage (ndma of them, 0 or 8), after even ones the
+        // fragment reads of substep `next` into (naf, nbf) (next >= 0; B's four first, which the
+        // next block's first MFMAs need, then A's).  Spread out like this neither the texture
+        // path nor the LDS queue backs up into this wave's MFMA issue: the same reads in one burst
+        // between blocks cost the GEMM about 3 %.  sched_barrier holds every operation in its slot.
+        auto mfma_block = [&](const bf16x8* af, const bf16x8* bfr, const Dma& d, int q0, int ndma,
+                              const char* sa, const char* sb, int next, bf16x8* naf, bf16x8* nbf) {
 #pragma unroll
             for (int g = 0; g < 16; ++g) {
                 const int i = g >> 2, j = g & 3;
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[j], af[i], acc[i][j], 0, 0, 0);
-                if (ndma > 0 && (g + 1) % (16 / ndma) == 0) {
-                    __builtin_amdgcn_sched_barrier(0);
-                    dma_op(d, q0 + (g + 1) / (16 / ndma) - 1);
-                    __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_sched_barrier(0);
+                if (ndma > 0 && (g & 1) == 1)
+                    dma_op(d, q0 + (g >> 1));
+                if (next >= 0 && (g & 1) == 0) {
+                    const int r = g >> 1;
+                    if (r < 4)
+                        nbf[r] = *reinterpret_cast<const bf16x8*>(sb + b_off[next] + r * 4096);
+                    else
+                        naf[r - 4] = *reinterpret_cast<const bf16x8*>(sa + a_off[next] + (r - 4) * 4096);
                 }
+                __builtin_amdgcn_sched_barrier(0);
             }
         };
         // One K step out of stage (sa, sb) while the loads of the next step fill the other stage:
-        // all 16 DMA operations go out during the first two substeps, which leaves the last two
-        // (1024 MFMA cycles) for them to land before the next barrier.
+        // the first substep's fragments are read in one burst after the step's barrier (nothing
+        // else is ready), each later substep's during the block before it.  All 16 DMA operations
+        // go out during the first two blocks, which leaves the last two (1024 MFMA cycles) for
+        // them to land before the next barrier.
         auto compute_bf16 = [&](const char* sa, const char* sb, const Dma& d) {
             bf16x8 a0[4], b0[4], a1[4], b1[4];
             load_frags(sa, sb, 0, a0, b0);
-            load_frags(sa, sb, 1, a1, b1);
             __builtin_amdgcn_sched_barrier(0);
-            mfma_block(a0, b0, d, 0, 8);
-            __builtin_amdgcn_sched_barrier(0);
-            load_frags(sa, sb, 2, a0, b0);
-            __builtin_amdgcn_sched_barrier(0);
-            mfma_block(a1, b1, d, 8, 8);
-            __builtin_amdgcn_sched_barrier(0);
-            load_frags(sa, sb, 3, a1, b1);
-            __builtin_amdgcn_sched_barrier(0);
-            mfma_block(a0, b0, d, 0, 0);
-            __builtin_amdgcn_sched_barrier(0);
-            mfma_block(a1, b1, d, 0, 0);
+            mfma_block(a0, b0, d, 0, 8, sa, sb, 1, a1, b1);
+            mfma_block(a1, b1, d, 8, 8, sa, sb, 2, a0, b0);
+            mfma_block(a0, b0, d, 0, 0, sa, sb, 3, a1, b1);
+            mfma_block(a1, b1, d, 0, 0, sa, sb, -1, nullptr, nullptr);
             __builtin_amdgcn_sched_barrier(0);
         };
         // FP8: a lane's fragment of substep kk is its row's 32 bytes at k bytes [64 kk + 32 fh, +32),
         // two chunks; a K step is two substeps of 16 v_mfma_f32_32x32x64_f8f6f4 (E4M3 operands: both
         // format fields 0; no block scales), in rows i of four MFMAs that share A fragment i.  The
-        // B fragments of both substeps stay in registers; the A fragments stream, each read one row
-        // of MFMAs ahead (80 VGPRs of fragments instead of 128, which keeps the fused kernel within
-        // the VGPR budget it shares with the copy kernel beside it).  The 16 DMA operations of the
+        // B fragments of both substeps stay in registers (the second substep's read during the
+        // first, one per row of MFMAs); the A fragments stream, each read one row of MFMAs ahead (80
+        // VGPRs of fragments instead of 128, which keeps the fused kernel within the VGPR budget it
+        // shares with the copy kernel beside it).  The 16 DMA operations of the
         // next stage go out one per MFMA of the first substep -- the same spacing in time as the
         // bf16 step's -- which leaves the second substep for them to land.
         auto frag8 = [&](const char* base, const uint32_t* off, int kk, int i) {
@@ -677,9 +680,6 @@ __device__ __forceinline__ void gemm_body(KParams p)
             for (int j = 0; j < 4; ++j)
                 b0[j] = frag8(sb, b_off, 0, j);
             i32x8 ac = frag8(sa, a_off, 0, 0);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                b1[j] = frag8(sb, b_off, 1, j);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int st = 0; st < 2; ++st) {
@@ -697,6 +697,8 @@ __device__ __forceinline__ void gemm_body(KParams p)
                         if (st == 0) {
                             __builtin_amdgcn_sched_barrier(0);
                             dma_op(d, 4 * i + j);
+                            if (j == 1)
+                                b1[i] = frag8(sb, b_off, 1, i);   // the second substep's B, spread out
                             __builtin_amdgcn_sched_barrier(0);
                         }
                     }
