@@ -170,3 +170,15 @@ def test_fp8_inputs_full_size_square_workload():
     absab = np.einsum("ik,ik->i", np.abs(va), np.abs(vb))
     ok, bad = within_summation_error(got[ms, ns], c32, absab, cfg.K, scale)
     assert ok, bad
+
+
+def test_fp8_inputs_one_chunk_rows_and_empty_k():
+    # K = 16: every row is one 16-byte chunk, the rest of the 128-byte K step reads zeros
+    N, H, K, Nc, cb = 2, 70, 16, 90, 20
+    print("fp8-in K=16 and K=0", flush=True)
+    check_exact(N, H, K, Nc, cb, seed=107, schedules=({}, {"mode": "unfused"}, {"producer": "in_kernel"}))
+    # K = 0: the empty sum, C = 0
+    sd = [torch.empty((H, 0), dtype=torch.uint8, device=DEV) for _ in range(N)]
+    Bd = torch.empty((Nc, 0), dtype=torch.uint8, device=DEV)
+    C = run(sd, Bd, cb)
+    assert not torch.isnan(C.float()).any() and (C.float() == 0).all()
