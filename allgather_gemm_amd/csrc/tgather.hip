@@ -12,7 +12,9 @@
 //    nothing.
 // On gfx950 the staging tile is a workgroup's registers: each logical tile is moved as a sequence
 // of sub-tiles of NT * UPT * 16 bytes, a sub-tile being loaded whole into VGPRs (16 bytes per load,
-// UPT loads per lane in flight) and then stored.  The sub-tiles of all tiles of all ranks and
+// UPT loads per lane in flight) and then stored.  UPT is 8 (32 KiB sub-tiles), or 12 (48 KiB) when
+// that packs the rows fuller -- a row of 0.6 of the smaller sub-tile leaves 40 % of every lane's
+// loads idle.  The sub-tiles of all tiles of all ranks and
 // planes form one index space that the grid walks with a stride; the load/store overlap of the
 // ping/pong scheme comes from the many workgroups resident on each CU, whose loads run while
 // others store.  An LDS hop would add traffic and buy nothing for a copy.  The copy is byte-exact
@@ -26,8 +28,7 @@ namespace ag {
 namespace {
 
 constexpr int NT = 256;
-constexpr int UPT = 8;                        // 16-byte units per lane per sub-tile
-constexpr int SUB_BYTES = NT * UPT * 16;      // one sub-tile (32 KiB)
+constexpr int UPT_SMALL = 8, UPT_LARGE = 12;  // 16-byte units per lane per sub-tile (32 / 48 KiB)
 constexpr int WG_PER_CU = 16;
 
 // A rectangular family of identical logical tiles inside one (rank, plane) region: the full
@@ -46,6 +47,7 @@ struct TileClass {
 
 struct Plan {
     GatherDesc d;
+    int64_t sub_bytes;  // bytes per sub-tile, NT * UPT * 16
     TileClass cls[4];
     int ncls;
     int64_t subs_per_region;
@@ -113,7 +115,7 @@ __device__ __forceinline__ Interior interior_of(const SubTile& s)
 }
 
 // u / nu for u < 2^16, nu >= 1 (single-precision reciprocal plus one correction step); a sub-tile
-// has at most NT * UPT = 2048 units.
+// has at most NT * UPT_LARGE = 3072 units.
 __device__ __forceinline__ uint32_t div_small(uint32_t u, uint32_t nu, float rcp)
 {
     uint32_t q = (uint32_t)((float)u * rcp);
@@ -132,6 +134,7 @@ __device__ __forceinline__ uint32_t div_small(uint32_t u, uint32_t nu, float rcp
 constexpr int kStream = 2;            // cache policy "nt": the copy's lines are used once
 constexpr uint32_t kNowhere = 0xFFFFFFF0u;
 
+template <int UPT>
 __device__ __forceinline__ void copy_interior(const SubTile& s, const Interior& in, int tid)
 {
     const uint32_t U = (uint32_t)(s.rows * in.nu);
@@ -200,13 +203,14 @@ __device__ __forceinline__ void copy_edges(const SubTile& s, const Interior& in,
     }
 }
 
+template <int UPT>
 __global__ __launch_bounds__(NT) void tgather_vec_kernel(Plan P)
 {
     const int tid = threadIdx.x;
     for (int64_t q = blockIdx.x; q < P.total; q += gridDim.x) {
         const SubTile s = locate(P, q);
         const Interior in = interior_of(s);
-        copy_interior(s, in, tid);
+        copy_interior<UPT>(s, in, tid);
         copy_edges(s, in, tid, P.d.elem_size);
     }
 }
@@ -249,6 +253,7 @@ void add_class(Plan& P, int64_t count, int64_t ncols, int64_t row0, int64_t col0
     c.th = th;
     c.tw = tw;
     const int64_t twb = tw * esz;
+    const int64_t SUB_BYTES = P.sub_bytes;
     if (twb <= SUB_BYTES) {
         c.scn = 1;
         c.scw = tw;
@@ -285,25 +290,44 @@ hipError_t launch_tgather(const GatherDesc& d, hipStream_t stream)
         if (e != hipSuccess)
             return e;
     }
-    Plan P{};
-    P.d = d;
-    const int64_t vr = std::min(d.valid_rows, d.H), vc = std::min(d.valid_cols, d.W);
-    const int64_t nrf = d.H / vr, hr = d.H - nrf * vr;        // full row tiles, ragged height
-    const int64_t ncf = d.W / vc, wr = d.W - ncf * vc;        // full column tiles, ragged width
-    add_class(P, nrf * ncf, ncf, 0, 0, vr, vc);
-    add_class(P, wr > 0 ? nrf : 0, 1, 0, ncf * vc, vr, wr);
-    add_class(P, hr > 0 ? ncf : 0, ncf, nrf * vr, 0, hr, vc);
-    add_class(P, (hr > 0 && wr > 0) ? 1 : 0, 1, nrf * vr, ncf * vc, hr, wr);
-    P.total = (int64_t)d.nranks * d.planes * P.subs_per_region;
+    // the plan for either sub-tile size; the larger one only if it packs the rows at least 10 %
+    // fuller (it holds 50 % more VGPRs per lane, so fewer workgroups fit on a CU)
+    auto make_plan = [&](int upt) {
+        Plan P{};
+        P.d = d;
+        P.sub_bytes = (int64_t)NT * upt * 16;
+        const int64_t vr = std::min(d.valid_rows, d.H), vc = std::min(d.valid_cols, d.W);
+        const int64_t nrf = d.H / vr, hr = d.H - nrf * vr;        // full row tiles, ragged height
+        const int64_t ncf = d.W / vc, wr = d.W - ncf * vc;        // full column tiles, ragged width
+        add_class(P, nrf * ncf, ncf, 0, 0, vr, vc);
+        add_class(P, wr > 0 ? nrf : 0, 1, 0, ncf * vc, vr, wr);
+        add_class(P, hr > 0 ? ncf : 0, ncf, nrf * vr, 0, hr, vc);
+        add_class(P, (hr > 0 && wr > 0) ? 1 : 0, 1, nrf * vr, ncf * vc, hr, wr);
+        P.total = (int64_t)d.nranks * d.planes * P.subs_per_region;
+        return P;
+    };
+    Plan P = make_plan(UPT_SMALL);
     bool aligned = ((d.W * d.elem_size) % 16) == 0 && ((uintptr_t)d.dst % 16) == 0;
     for (int r = 0; r < d.nranks; ++r)
         aligned = aligned && ((uintptr_t)d.src[r] % 16) == 0;
     P.vec = aligned ? 1 : 0;
+    int upt = UPT_SMALL;
+    if (P.vec) {
+        const Plan L = make_plan(UPT_LARGE);
+        // fill = payload / (sub-tiles * sub-tile bytes): the payload is common to both plans
+        if (11 * L.total * L.sub_bytes <= 10 * P.total * P.sub_bytes) {
+            P = L;
+            P.vec = 1;
+            upt = UPT_LARGE;
+        }
+    }
     const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(P.total, (int64_t)g_num_cus * WG_PER_CU));
-    if (P.vec)
-        tgather_vec_kernel<<<grid, NT, 0, stream>>>(P);
-    else
+    if (!P.vec)
         tgather_elem_kernel<<<grid, NT, 0, stream>>>(P);
+    else if (upt == UPT_LARGE)
+        tgather_vec_kernel<UPT_LARGE><<<grid, NT, 0, stream>>>(P);
+    else
+        tgather_vec_kernel<UPT_SMALL><<<grid, NT, 0, stream>>>(P);
     return hipGetLastError();
 }
 
