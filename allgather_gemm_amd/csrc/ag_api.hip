@@ -61,9 +61,14 @@ int current_ws(Workspace** out)
     if (!w.ctl) {
         AG_HIP(hipMalloc(&w.ctl, 8 * sizeof(uint32_t)), "hipMalloc(control)");
         AG_HIP(hipMemset(w.ctl, 0, 8 * sizeof(uint32_t)), "hipMemset(control)");
-        AG_HIP(hipEventCreateWithFlags(&w.last, hipEventDisableTiming), "hipEventCreate");
-        AG_HIP(hipEventCreateWithFlags(&w.fork, hipEventDisableTiming), "hipEventCreate");
-        AG_HIP(hipEventCreateWithFlags(&w.join, hipEventDisableTiming), "hipEventCreate");
+        // The workspace's events only order this library's kernels against each other on this
+        // device (every kernel's own end-of-kernel release makes its writes visible to later
+        // kernels); nothing on the host waits on them.  Without the system-scope fences each of
+        // their markers idles the GPU about 1 us less between kernels (about 5 instead of 6).
+        const unsigned ev_flags = hipEventDisableTiming | hipEventDisableSystemFence;
+        AG_HIP(hipEventCreateWithFlags(&w.last, ev_flags), "hipEventCreate");
+        AG_HIP(hipEventCreateWithFlags(&w.fork, ev_flags), "hipEventCreate");
+        AG_HIP(hipEventCreateWithFlags(&w.join, ev_flags), "hipEventCreate");
         AG_HIP(hipStreamCreateWithFlags(&w.side, hipStreamNonBlocking), "hipStreamCreate");
     }
     *out = &w;
