@@ -115,6 +115,31 @@ def test_edge_shapes_full_check(N, H, K, Nc, cb, local):
     assert ag.check()[0] == ag.AG_OK
 
 
+def test_largest_supported_k_is_exact():
+    """K = 2^21, the largest the library accepts: a full 256-row tile then spans 1 GiB of A (its
+    buffer offsets are 32-bit) and one workgroup runs 32768 K steps.  Entries in {-1, 0, 1} keep every
+    partial sum an integer of magnitude at most 2^21, exact in fp32 in any order, so C must equal the
+    oracle's rounding bit for bit in every schedule, and the gathered A the shards' bytes."""
+    N, H, K, Nc, cb = 2, 128, 1 << 21, 24, 50
+    print("AG-GEMM largest K: N=%d H=%d K=%d Nc=%d" % (N, H, K, Nc), flush=True)
+    shards, B = workloads.make_ag_gemm_integers(N, H, K, Nc, seed=23, lim=1)
+    A_ref, C32 = oracle.ag_gemm([u16(s) for s in shards], u16(B))
+    assert np.abs(C32).max() <= K
+    want = oracle.f32_to_bf16(C32)
+    sd, Bd = [s.to(DEV) for s in shards], B.to(DEV)
+    del shards
+    a_out = torch.empty((N * H, K), dtype=torch.bfloat16, device=DEV)
+    for kw in [{"producer": p} for p in PRODUCERS] + [{"mode": "unfused"}, {"local_rank": 1}]:
+        a_out.fill_(float("nan"))
+        C = run(sd, Bd, cb, a_out=a_out, **kw)
+        assert np.array_equal(u16(C), want), kw
+        if kw.get("mode") != "unfused":
+            assert np.array_equal(u16(a_out), A_ref), kw
+    C = run(sd, Bd, cb, a_out=a_out, mode="plain_gemm")
+    assert np.array_equal(u16(C), want)
+    assert ag.check()[0] == ag.AG_OK
+
+
 def test_zero_k_gives_zero():
     shards = [torch.empty((16, 0), dtype=torch.bfloat16, device=DEV) for _ in range(2)]
     B = torch.empty((24, 0), dtype=torch.bfloat16, device=DEV)
