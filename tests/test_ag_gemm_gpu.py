@@ -140,6 +140,24 @@ def test_largest_supported_k_is_exact():
     assert ag.check()[0] == ag.AG_OK
 
 
+def test_largest_supported_shard_count():
+    """N = 64 shards, the most the library carries in its kernel arguments, the local shard the last
+    one; 20-row shards (tiles straddle up to 13 shards), 3 chunks per shard, ragged Nc."""
+    N, H, K, Nc, cb, local = 64, 20, 96, 136, 7, 63
+    print("AG-GEMM N=%d H=%d K=%d Nc=%d cb=%d local=%d" % (N, H, K, Nc, cb, local), flush=True)
+    A, shards, B = workloads.make_ag_gemm_shapes(N, H, K, Nc, seed=64)
+    A_ref, C32 = oracle.ag_gemm([u16(s) for s in shards], u16(B))
+    sd, Bd = to_dev(A, shards, B)
+    C_u = run(sd, Bd, cb, mode="unfused")
+    assert_close_to_oracle(C_u, C32, "unfused")
+    for producer in PRODUCERS:
+        a_out = torch.full((N * H, K), float("nan"), dtype=torch.bfloat16, device=DEV)
+        C_f = run(sd, Bd, cb, local_rank=local, a_out=a_out, producer=producer)
+        assert np.array_equal(u16(a_out), A_ref), producer
+        assert torch.equal(C_f.view(torch.int16), C_u.view(torch.int16)), producer
+    assert ag.check()[0] == ag.AG_OK
+
+
 def test_zero_k_gives_zero():
     shards = [torch.empty((16, 0), dtype=torch.bfloat16, device=DEV) for _ in range(2)]
     B = torch.empty((24, 0), dtype=torch.bfloat16, device=DEV)

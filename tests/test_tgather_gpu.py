@@ -71,6 +71,16 @@ def test_ragged_fp32_gather_workload(bits):
     run_and_compare(shards, cfg.D, cfg.H, cfg.W, cfg.valid_rows, cfg.valid_cols)
 
 
+@pytest.mark.parametrize("dtype,W", [(torch.float16, 64),    # 128-byte rows: 16-byte vector path
+                                     (torch.float16, 70),    # 140-byte rows: element path
+                                     (torch.uint8, 70)])
+def test_largest_supported_rank_count(dtype, W):
+    """64 source ranks, the most the library carries; two planes, ragged tiles."""
+    N, D, H = 64, (2, 1, 1), 9
+    shards = workloads.make_tgather(N, D, H, W, dtype, seed=64)
+    run_and_compare(shards, D, H, W, 4, 33)
+
+
 @pytest.mark.parametrize("dtype,count", [(torch.float32, 256), (torch.int32, 4096), (torch.uint8, 512)])
 def test_page_matrix_basic(dtype, count):
     """§九 basic: per-rank [1,1,1,1,count], value i + rank*10000 (wrapping for uint8)."""
