@@ -939,7 +939,10 @@ __global__ __launch_bounds__(NT) void producer_kernel(KParams p, uint32_t* ctr, 
 // units past a piece's end read zeros and store nothing, so no lane takes a branch); the flags of
 // those chunks are raised, the piece counters start past them and the per-chunk piece counts at
 // zero.  Nothing reads the flags, counters or copied rows before this kernel has ended.
-constexpr int FILL_PIECES = 4;
+// The kernel is short and latency-bound, so it is spread wide: one piece per workgroup copies the
+// square workload's 16 MiB first wave in about 9 us, four per workgroup took 13.5 us, two 10.6 us,
+// and half a piece per workgroup is no faster than one.
+constexpr int FILL_PIECES = 1;
 
 __global__ __launch_bounds__(NT) void fill_kernel(KParams p)
 {
