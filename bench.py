@@ -65,6 +65,10 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="target length of the CPU sample")
     ap.add_argument("--headline-only", action="store_true",
                     help="only the headline steps (plus one calibration copy): for rocprofv3 runs")
+    ap.add_argument("--workload", default="ag_gemm_8192x8192x8192",
+                    help="with --headline-only: the AG-GEMM workload of the steps (a name from workloads.py)")
+    ap.add_argument("--mode", default="fused", choices=("fused", "unfused", "plain_gemm"),
+                    help="with --headline-only: the schedule of the steps")
     ap.add_argument("--tgather-only", action="store_true",
                     help="only TGATHER on its two workloads, --steps calls each: for rocprofv3 runs")
     ap.add_argument("--fp8-only", action="store_true",
@@ -349,7 +353,14 @@ def main():
         return A, shards, B, sd, Bd, C, a_gath
 
     cfg = workloads.AG_SQUARE
+    mode = "fused"
+    if args.headline_only:
+        # a rocprofv3 run of another workload or schedule: the same steps, nothing else
+        cfg = workloads.AG_CONFIGS[args.workload]
+        mode = args.mode
     A, shards, B, sd, Bd, C, a_gath = load(cfg)
+    if mode == "plain_gemm":
+        a_gath.copy_(A.to(dev))   # the plain GEMM reads the gathered A as its input
 
     # headline: K back-to-back fused steps, the GEMM kernel of each timed by the library's events
     kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -357,13 +368,13 @@ def main():
         k[0].record(stream)
         k[1].record(stream)
     for _ in range(args.warmup):
-        ag.ag_gemm(sd, Bd, cfg.cb, C=C, a_out=a_gath)
+        ag.ag_gemm(sd, Bd, cfg.cb, C=C, a_out=a_gath, mode=mode)
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for i in range(args.steps):
-        ag.ag_gemm(sd, Bd, cfg.cb, C=C, a_out=a_gath, gemm_events=kev[i])
+        ag.ag_gemm(sd, Bd, cfg.cb, C=C, a_out=a_gath, gemm_events=kev[i], mode=mode)
     end.record(stream)
     torch.cuda.synchronize()
     ms_fused = start.elapsed_time(end) / args.steps
@@ -377,12 +388,13 @@ def main():
 
     # how long the fused GEMM's tiles waited on chunk flags: 10 more calls, outside the timed steps
     wst = torch.zeros(4, dtype=torch.int64, device=dev)
-    nw = 10
+    nw = 10 if mode == "fused" else 0
     for _ in range(nw):
         ag.ag_gemm(sd, Bd, cfg.cb, C=C, a_out=a_gath, wait_stats=wst)
     torch.cuda.synchronize()
+    nw = max(nw, 1)
     ticks, waits, copied, skipped = (int(v) for v in wst.cpu().tolist())
-    grid = min(ag_cus(torch), (cfg.M // 256) * (cfg.Nc // 256))
+    grid = min(ag_cus(torch), ((cfg.M + 255) // 256) * ((cfg.Nc + 255) // 256))
     fused_waits = {
         "calls": nw, "workgroups": grid,
         "wait_us_per_call_summed_over_workgroups": round(ticks / 100.0 / nw, 2),
@@ -391,6 +403,8 @@ def main():
         "pieces_copied_by_waiting_tiles_per_call": copied / nw,
         "pieces_per_call": cfg.N * ((cfg.H + cfg.cb - 1) // cfg.cb) * ((cfg.cb * cfg.K * 2 + 16383) // 16384),
     }
+    if mode != "fused":
+        fused_waits = None
 
     if args.headline_only:
         # one copy of known size, for scaling the memory counters of a profiled run: 256 MiB read
@@ -400,7 +414,8 @@ def main():
         Scrubber(torch, dev)()
         ag.tgather(shs, 4096, 4096, dst=dst)
         torch.cuda.synchronize()
-        print(json.dumps({"headline_only": True, "ms_per_step": round(ms_fused, 5),
+        print(json.dumps({"headline_only": True, "workload": cfg.name, "mode": mode,
+                          "ms_per_step": round(ms_fused, 5),
                           "gemm_kernel_ms": round(gemm_kernel_ms, 5), "TFLOP/s": round(tflops, 2),
                           "fused_waits": fused_waits,
                           "calibration_copy_bytes_each_way": 8 * 4096 * 4096 * 2}), flush=True)
