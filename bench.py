@@ -244,7 +244,7 @@ def cpu_baseline(cfg, shards, B, target_s):
             break
         rows = min(cfg.M, max(rows * 2, int(rows * target_s / max(dt, 1e-3) * 1.05)))
     flops = 2.0 * rows * cfg.Nc * cfg.K
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    threads = oracle.num_threads()
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": "%d full rows x %d columns of C of the %s workload (%.1f s; oracle built gcc -O3 "
                       "-fopenmp -ffp-contract=off, no -march)" % (rows, cfg.Nc, cfg.name, dt)}

@@ -25,6 +25,11 @@ _i64 = ctypes.c_int64
 _vp = ctypes.c_void_p
 
 
+def num_threads() -> int:
+    """Threads the oracle's OpenMP loops use (OMP_NUM_THREADS when set, else the runtime's default)."""
+    return int(lib().oracle_num_threads())
+
+
 def build(force: bool = True) -> str:
     """Compile oracle.c with gcc into liboracle.so next to it and return its path."""
     if force or not os.path.exists(_SO):
@@ -42,6 +47,8 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(_SO):
             build()
         L = ctypes.CDLL(_SO)
+        L.oracle_num_threads.argtypes = []
+        L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
         L.oracle_bf16_to_f32.restype = ctypes.c_float
         L.oracle_f32_to_bf16_rne.argtypes = [ctypes.c_float]

@@ -16,6 +16,9 @@
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 float oracle_bf16_to_f32(uint16_t h)
 {
@@ -501,4 +504,13 @@ int oracle_ag_gemm_pivoted(const uint16_t *const *shards, int nshards, int64_t M
     free(p.published);
     free(need);
     return rc;
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }

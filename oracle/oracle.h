@@ -145,6 +145,10 @@ int oracle_ag_gemm_pivoted(const uint16_t *const *shards, int nshards, int64_t M
                            int64_t group_m, int local_rank, uint16_t *A_prime, float *C,
                            int64_t *stats);
 
+/* Threads the OpenMP loops above use (1 in a build without OpenMP): what a timing of the oracle
+ * reports as its core count. */
+int oracle_num_threads(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -178,6 +178,7 @@ static int reduce_cases(void)
 
 int main(void)
 {
+    CHECK(oracle_num_threads() >= 1);
     if (gemm_cases() || ag_gemm_cases() || tgather_cases() || conversion_cases() || reduce_cases())
         return 1;
     printf("OK\n");
