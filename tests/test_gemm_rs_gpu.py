@@ -60,6 +60,23 @@ def test_gemm_rs_exact_integers_every_rank_fused_and_unfused():
             assert np.array_equal(out, out_ref), (local, fused)
 
 
+@pytest.mark.parametrize("N,H,local", [(1, 300, 0),     # one rank: the reduction is its own block
+                                       (64, 8, 0),      # the most ranks the library carries
+                                       (64, 8, 63)])
+def test_gemm_rs_exact_integers_rank_count_extremes(N, H, local):
+    K, Nc = 48, 40
+    print("gemm_rs exact N=%d H=%d local=%d" % (N, H, local), flush=True)
+    shards, B = workloads.make_ag_gemm_integers(1, N * H, K, Nc, seed=94, lim=2)
+    A = shards[0]
+    peers, _ = workloads.make_ag_gemm_integers(N, H, Nc, 8, seed=95, lim=30)
+    recv = [None if j == local else peers[j] for j in range(N)]
+    P_ref, out_ref = oracle.gemm_rs(u16(A), u16(B), [None if r is None else u16(r) for r in recv], local)
+    for fused in (True, False):
+        P, out = run(A, B, recv, local, fused)
+        assert np.array_equal(P, P_ref), fused
+        assert np.array_equal(out, out_ref), fused
+
+
 def check_random(cfg, sample=None):
     A, B, recv = workloads.make_gemm_rs(cfg)
     H = cfg.H
