@@ -172,6 +172,28 @@ def test_fp8_inputs_full_size_square_workload():
     assert ok, bad
 
 
+def test_fp8_inputs_largest_supported_k():
+    # K = 2^21 codes per row (2 MiB): a full 256-row tile spans 512 MiB of A; values in {-1, 0, 1}
+    # keep every partial sum an integer of magnitude at most 2^21, exact in any order
+    N, H, K, Nc, cb = 2, 128, 1 << 21, 24, 50
+    print("fp8-in largest K", flush=True)
+    shards, B = workloads.make_ag_gemm_fp8_integers(N, H, K, Nc, seed=108, lim=1)
+    _, C32 = oracle.ag_gemm(images(shards), oracle.e4m3fn_to_bf16(b8(B)))
+    assert np.abs(C32).max() <= K
+    want = oracle.f32_to_bf16(C32)
+    A_bytes = gathered(shards)
+    sd = [s.to(DEV) for s in shards]
+    Bd = B.to(DEV)
+    del shards
+    a_out = torch.empty((N * H, K), dtype=torch.uint8, device=DEV)
+    for kw in ({}, {"producer": "in_kernel"}, {"mode": "unfused"}, {"local_rank": 1}):
+        a_out.fill_(0x7F)
+        got = u16(run(sd, Bd, cb, a_out=a_out, **kw))
+        assert np.array_equal(got, want), kw
+        if kw.get("mode") != "unfused":
+            assert np.array_equal(b8(a_out), A_bytes), kw
+
+
 def test_fp8_inputs_one_chunk_rows_and_empty_k():
     # K = 16: every row is one 16-byte chunk, the rest of the 128-byte K step reads zeros
     N, H, K, Nc, cb = 2, 70, 16, 90, 20
