@@ -148,3 +148,21 @@ def test_unaligned_base_pointers_take_element_path():
     ag.tgather(shards, 5, 9, dst=dst)
     torch.cuda.synchronize()
     assert np.array_equal(np_bytes(dst), oracle_gather(src_cpu, (1, 1, 1), 32, 64))
+
+
+@pytest.mark.slow
+def test_sub_tile_spans_capped_and_destination_beyond_4_gib():
+    """Rows 2 MiB apart and 16-byte-wide tiles 1100 rows tall: a sub-tile of up to 2048 such rows
+    would span more than the 2 GiB its 32-bit buffer offsets reach, so the plan cuts it at 1024 rows.
+    Two 2.2 GiB ranks fill a 4.4 GiB destination, so the second rank's rows lie beyond 4 GiB."""
+    N, D, H, W = 2, (1, 1, 1), 1100, 2 << 20
+    print("tgather large: N=%d H=%d W=%d uint8" % (N, H, W), flush=True)
+    shards = workloads.make_tgather(N, D, H, W, torch.uint8, seed=77, bits=True)
+    expect = oracle_gather(shards, D, H, W)
+    sd = [s.to(DEV) for s in shards]
+    del shards
+    dst = torch.empty((1, 1, 1, N * H, W), dtype=torch.uint8, device=DEV)
+    ag.tgather(sd, H, 16, dst=dst)
+    torch.cuda.synchronize()
+    del sd
+    assert np.array_equal(np_bytes(dst), expect)
