@@ -140,6 +140,28 @@ def test_largest_supported_k_is_exact():
     assert ag.check()[0] == ag.AG_OK
 
 
+@pytest.mark.slow
+def test_gathered_a_beyond_4_gib():
+    """A 4.5 GiB gathered A (2304 rows of 2 MiB): pieces, chunk rows and tile rows sit beyond 4 GiB,
+    so every offset into it must be 64-bit.  Integer inputs in {-1, 0, 1}: C exact, bit for bit."""
+    N, H, K, Nc, cb = 2, 1152, 1 << 20, 24, 100
+    print("AG-GEMM gathered A beyond 4 GiB: N=%d H=%d K=%d Nc=%d" % (N, H, K, Nc), flush=True)
+    shards, B = workloads.make_ag_gemm_integers(N, H, K, Nc, seed=29, lim=1)
+    C32 = oracle.ag_gemm_fast([u16(s) for s in shards], u16(B))
+    want = oracle.f32_to_bf16(C32)
+    sd, Bd = [s.to(DEV) for s in shards], B.to(DEV)
+    del shards
+    a_out = torch.empty((N * H, K), dtype=torch.bfloat16, device=DEV)
+    for kw in ({}, {"producer": "in_kernel"}, {"mode": "unfused"}):
+        a_out.fill_(float("nan"))
+        C = run(sd, Bd, cb, a_out=a_out, **kw)
+        assert np.array_equal(u16(C), want), kw
+        if kw.get("mode") != "unfused":
+            for r in range(N):     # the gathered A, rank by rank, against the shards' bits
+                assert torch.equal(a_out[r * H:(r + 1) * H].view(torch.int16), sd[r].view(torch.int16)), (kw, r)
+    assert ag.check()[0] == ag.AG_OK
+
+
 def test_largest_supported_shard_count():
     """N = 64 shards, the most the library carries in its kernel arguments, the local shard the last
     one; 20-row shards (tiles straddle up to 13 shards), 3 chunks per shard, ragged Nc."""

@@ -91,9 +91,12 @@ def make_ag_gemm_shapes(N: int, H: int, K: int, Nc: int, seed: int = 0, a_std: f
 def make_ag_gemm_integers(N: int, H: int, K: int, Nc: int, seed: int = 0, lim: int = 3):
     """Shards and B with integer entries in [-lim, lim] (exact in bf16): with small K every partial
     sum is an integer far below 2^24, so an fp32 sum is exact in any order.  Returns (shards, B)."""
+    assert 0 <= lim < 128
     g = torch.Generator().manual_seed(seed)
-    shards = [torch.randint(-lim, lim + 1, (H, K), generator=g).to(torch.bfloat16) for _ in range(N)]
-    B = torch.randint(-lim, lim + 1, (Nc, K), generator=g).to(torch.bfloat16)
+    # int8 draws: the same values as int64 ones from the same generator, at an eighth of the memory
+    shards = [torch.randint(-lim, lim + 1, (H, K), generator=g, dtype=torch.int8).to(torch.bfloat16)
+              for _ in range(N)]
+    B = torch.randint(-lim, lim + 1, (Nc, K), generator=g, dtype=torch.int8).to(torch.bfloat16)
     return shards, B
 
 
@@ -123,9 +126,11 @@ def make_ag_gemm_fp8_integers(N: int, H: int, K: int, Nc: int, seed: int = 0, li
     """FP8 inputs with integer values in [-lim, lim] (exact in E4M3 for lim <= 16): every fp32
     partial sum is an integer below 2^24 for K * lim^2 < 2^24, exact in any order.  Returns
     (shards, B) as uint8 codes."""
+    assert 0 <= lim <= 16
     g = torch.Generator().manual_seed(seed)
-    shards = [to_e4m3fn_codes(torch.randint(-lim, lim + 1, (H, K), generator=g).float()) for _ in range(N)]
-    B = to_e4m3fn_codes(torch.randint(-lim, lim + 1, (Nc, K), generator=g).float())
+    shards = [to_e4m3fn_codes(torch.randint(-lim, lim + 1, (H, K), generator=g, dtype=torch.int8).float())
+              for _ in range(N)]
+    B = to_e4m3fn_codes(torch.randint(-lim, lim + 1, (Nc, K), generator=g, dtype=torch.int8).float())
     return shards, B
 
 
