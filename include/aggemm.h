@@ -138,7 +138,7 @@ int ag_gemm_ex(const void *const *shards, int32_t N, int64_t M, int64_t K, const
  *                        do not divide H / W; values above H / W mean one tile spans the plane.
  *                        The result does not depend on them (a copy is exact); the work split does.
  *   elem_size            1, 2, 4 or 8 bytes.
-  * Any extent of 0 enqueues nothing ([TGATH] 7.4).  16-byte aligned pointers with
+ * Any extent of 0 enqueues nothing ([TGATH] 7.4).  16-byte aligned pointers with
  * W * elem_size % 16 == 0 take the 16-byte vector path; anything else a slower element path.
  */
 int tgather(const void *const *shards, int32_t N, void *dst, int64_t D0, int64_t D1, int64_t D2,
@@ -171,8 +171,8 @@ int tgather_ex(const void *const *shards, int32_t N, void *dst, int64_t D0, int6
  *   mode              AG_RS_FUSED: a reducing kernel on a second stream starts on each GEMM tile
  *                     row of the block as soon as that row's tiles are written; AG_RS_UNFUSED: the
  *                     GEMM, then the reduction.  Both give bitwise the same P and out.
- * M % N == 0, K % 8 == 0, Nc % 8 == 0; 16-byte aligned pointers.  A wait that gave up (10 s) is
- * reported by ag_check.
+ * M % N == 0, K % 8 == 0, Nc % 8 == 0; 16-byte aligned pointers.  K > 2^21 or Nc > 2^26 returns
+ * AG_EUNSUPPORTED.  A wait that gave up (10 s) is reported by ag_check.
  */
 #define AG_RS_FUSED    0
 #define AG_RS_UNFUSED  1
