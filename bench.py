@@ -67,8 +67,9 @@ def parse():
                     help="only the headline steps (plus one calibration copy): for rocprofv3 runs")
     ap.add_argument("--workload", default="ag_gemm_8192x8192x8192",
                     help="with --headline-only: the AG-GEMM workload of the steps (a name from workloads.py)")
-    ap.add_argument("--mode", default="fused", choices=("fused", "unfused", "plain_gemm"),
-                    help="with --headline-only: the schedule of the steps")
+    ap.add_argument("--mode", default="fused", choices=("fused", "fused_in_kernel", "unfused", "plain_gemm"),
+                    help="with --headline-only: the schedule of the steps (fused_in_kernel: the fused "
+                         "schedule with the GEMM's own workgroups copying)")
     ap.add_argument("--tgather-only", action="store_true",
                     help="only TGATHER on its two workloads, --steps calls each: for rocprofv3 runs")
     ap.add_argument("--fp8-only", action="store_true",
@@ -361,6 +362,7 @@ def main():
     A, shards, B, sd, Bd, C, a_gath = load(cfg)
     if mode == "plain_gemm":
         a_gath.copy_(A.to(dev))   # the plain GEMM reads the gathered A as its input
+    step_kw = {"producer": "in_kernel"} if mode == "fused_in_kernel" else {"mode": mode}
 
     # headline: K back-to-back fused steps, the GEMM kernel of each timed by the library's events
     kev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -368,13 +370,13 @@ def main():
         k[0].record(stream)
         k[1].record(stream)
     for _ in range(args.warmup):
-        ag.ag_gemm(sd, Bd, cfg.cb, C=C, a_out=a_gath, mode=mode)
+        ag.ag_gemm(sd, Bd, cfg.cb, C=C, a_out=a_gath, **step_kw)
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for i in range(args.steps):
-        ag.ag_gemm(sd, Bd, cfg.cb, C=C, a_out=a_gath, gemm_events=kev[i], mode=mode)
+        ag.ag_gemm(sd, Bd, cfg.cb, C=C, a_out=a_gath, gemm_events=kev[i], **step_kw)
     end.record(stream)
     torch.cuda.synchronize()
     ms_fused = start.elapsed_time(end) / args.steps
@@ -388,9 +390,9 @@ def main():
 
     # how long the fused GEMM's tiles waited on chunk flags: 10 more calls, outside the timed steps
     wst = torch.zeros(4, dtype=torch.int64, device=dev)
-    nw = 10 if mode == "fused" else 0
+    nw = 10 if mode in ("fused", "fused_in_kernel") else 0
     for _ in range(nw):
-        ag.ag_gemm(sd, Bd, cfg.cb, C=C, a_out=a_gath, wait_stats=wst)
+        ag.ag_gemm(sd, Bd, cfg.cb, C=C, a_out=a_gath, wait_stats=wst, **step_kw)
     torch.cuda.synchronize()
     nw = max(nw, 1)
     ticks, waits, copied, skipped = (int(v) for v in wst.cpu().tolist())
@@ -403,7 +405,7 @@ def main():
         "pieces_copied_by_waiting_tiles_per_call": copied / nw,
         "pieces_per_call": cfg.N * ((cfg.H + cfg.cb - 1) // cfg.cb) * ((cfg.cb * cfg.K * 2 + 16383) // 16384),
     }
-    if mode != "fused":
+    if mode not in ("fused", "fused_in_kernel"):
         fused_waits = None
 
     if args.headline_only:
